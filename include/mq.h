@@ -1,0 +1,155 @@
+/*
+ * mq.h — prefill matmul over GGUF block-quantized weights on AMD MI355X (gfx950).
+ *
+ * The operation (minfer "05 · 8p — Persistent f16 weight cache + fused
+ * dequant-in-GEMM", §2 Principle): Y = X·Wᵀ with X the f16 activations of
+ * M prefill tokens [M × K], W a quantized weight of N output rows [N × K]
+ * and Y in f32 [M × N].  Two shapes of the same product are offered:
+ *
+ *   1. the persistent f16 cache: mq_dequant_to_f16 decodes W once (at load
+ *      time) into an f16 matrix with an optionally padded row stride, and
+ *      mq_gemm_f16cache multiplies X by it (f16 products, f32 accumulation);
+ *   2. the fused kernel: mq_gemm_fused reads the quantized bytes of W inside
+ *      the GEMM and expands them to f16 on the fly, for callers that cannot
+ *      spend 2 bytes per weight of extra device memory.
+ *
+ * Both feed the contraction the same f16 values (§3.3: the fused expansion
+ * follows the standalone decode's rounding path bit for bit).
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates device memory, never frees, never synchronizes the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it in call order and returns immediately; buffers
+ *     must stay alive until the stream has passed the call.
+ *   - Arguments are validated before anything is enqueued; on any error the
+ *     call returns a negative MQ_ERR_* code and has no side effect.
+ *   - Faults that happen while a kernel runs are reported by HIP at the
+ *     caller's next synchronization, not by these functions.
+ *   - Every function is thread-safe; calls on different streams may overlap.
+ *   - Weights must not change while an f16 cache built from them is in use
+ *     (the cache is derived state; minfer 05 · 8p §2: weights are immutable
+ *     after load).
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats, numbered as GGUF types (minfer's type_id 6 is Q5_0, page
+ * "79 · Phase-8 coverage batch", §3.6, which fixes the numbering).
+ *   MQ_Q8_0: 32 elements in 34 bytes   = f16 d, 32 × int8 q;        w = d·q
+ *   MQ_Q4_K: 256 elements in 144 bytes = f16 d, f16 dmin, 12 bytes of eight
+ *            6-bit scales + eight 6-bit mins, 128 bytes of 4-bit q;
+ *            w = d·sc·q − dmin·m per 32-element sub-block
+ *   MQ_Q6_K: 256 elements in 210 bytes = 128 B low 4 bits, 64 B high 2 bits
+ *            of 6-bit q, 16 × int8 scales, f16 d;  w = d·s·(q − 32)
+ * A quantized weight of N rows is N rows of K/block_elems blocks each, rows
+ * contiguous (row bytes = K/block_elems · block_bytes).  Q8_0 and Q6_K blocks
+ * are only 2-byte aligned inside a row (minfer 05 · 8p §2: alignment of a
+ * strided block is stride·g + offset); the library never issues a load that
+ * needs more. */
+enum {
+    MQ_Q8_0 = 8,
+    MQ_Q4_K = 12,
+    MQ_Q6_K = 14
+};
+
+/* Return codes. */
+enum {
+    MQ_OK = 0,
+    MQ_ERR_NULL = -1,      /* a required pointer is NULL */
+    MQ_ERR_FORMAT = -2,    /* unknown weight format */
+    MQ_ERR_SHAPE = -3,     /* M, N or K <= 0 or too large, or K not a multiple of the block */
+    MQ_ERR_LD = -4,        /* a leading dimension is too small or not a multiple of 8 */
+    MQ_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
+    MQ_ERR_WORKSPACE = -6, /* workspace missing or smaller than mq_gemm_workspace_bytes */
+    MQ_ERR_SPLIT = -7,     /* split_k outside 0..MQ_MAX_SPLIT_K */
+    MQ_ERR_HIP = -8        /* the HIP runtime rejected a launch; see mq_last_hip_error */
+};
+
+/* Limits checked by every entry point. */
+#define MQ_MAX_DIM (1 << 24)     /* M and N */
+#define MQ_MAX_K (1 << 21)       /* K and every leading dimension */
+#define MQ_MAX_SPLIT_K 16
+
+/* Elements per block of `fmt` (32, 256, 256), or MQ_ERR_FORMAT. */
+int mq_block_elems(int fmt);
+
+/* Bytes per block of `fmt` (34, 144, 210), or MQ_ERR_FORMAT. */
+int mq_block_bytes(int fmt);
+
+/* Bytes of one quantized row of K elements, or a negative MQ_ERR_* code when
+ * the format is unknown or K is not a positive multiple of the block. */
+int64_t mq_row_bytes(int fmt, int64_t K);
+
+/* Row stride (elements) of the f16 cache for an inner size K: K + 64 (one
+ * 128-byte line) when the f16 row size 2·K bytes is a multiple of 2048, else K
+ * (llama.cpp PR #57, Summary, second bullet: pad only when the row aliases at
+ * 2048 B).  Negative MQ_ERR_SHAPE when K <= 0 or K > MQ_MAX_K. */
+int64_t mq_f16cache_ld(int64_t K);
+
+/* Decode a quantized N×K weight into the f16 cache.
+ *   wq  : device, 16-byte aligned, N·mq_row_bytes(fmt, K) bytes, read only.
+ *   w16 : device, 16-byte aligned, N·ld f16 (uint16 bit patterns), written:
+ *         w16[n·ld + k] = f16 of weight (n, k) for k < K, +0 for K <= k < ld.
+ *   ld  : >= K, multiple of 8 (mq_f16cache_ld(K) is the padded choice).
+ * Each element is computed in f32 and rounded once to f16 (round to nearest
+ * even, subnormals kept, IEEE signed zeros kept): Q4_K as fl32(d·sc·q − dmin·m),
+ * Q6_K as (d·s)·(q − 32), Q8_0 as d·q (minfer 05 · 8p §3.2: float math, then
+ * one conversion to half).  The result is bit-identical to that definition.
+ * One kernel, one pass over the quantized bytes; HBM-bound. */
+int mq_dequant_to_f16(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
+                      void *stream);
+
+/* Workspace bytes the GEMM entry points need for this problem: 0 when the
+ * launch is not split along K, else split_k · M · N · 4 (one f32 partial plane
+ * per split, reduced in a fixed order so results are deterministic; Fucina
+ * "Eager GPU Offload Without A Compute Graph", F16/quantized linears: split-K
+ * for underfilled grids with caller-owned partial planes).
+ *   fmt     : 0 for mq_gemm_f16cache, else the weight format of mq_gemm_fused.
+ *   split_k : 0 = let the library choose (as the GEMM will with the same
+ *             arguments), 1 = no split, 2..MQ_MAX_SPLIT_K = forced.
+ * Negative MQ_ERR_* on invalid arguments. */
+int64_t mq_gemm_workspace_bytes(int fmt, int M, int N, int K, int split_k);
+
+/* Y[M×N] = X[M×K] · W16[N×K]ᵀ on the f16 cache.
+ *   X   : device f16, 16-byte aligned, row stride ldx (>= K, multiple of 8).
+ *   W16 : device f16, 16-byte aligned, row stride ldw (>= K, multiple of 8);
+ *         columns >= K are never read.
+ *   Y   : device f32, 16-byte aligned, row stride ldy (>= N); overwritten.
+ *   ws  : device workspace of ws_bytes >= mq_gemm_workspace_bytes(0, M, N, K,
+ *         split_k); may be NULL when that is 0.
+ *   K   : multiple of 8.
+ * f16 × f16 products are exact in f32; accumulation is f32 (MFMA).  Accuracy
+ * contract: |Y − X·Wᵀ| <= 1e-3·(|X|·|W|ᵀ) + 1e-5 per element. */
+int mq_gemm_f16cache(const uint16_t *X, int ldx, const uint16_t *W16, int ldw, float *Y,
+                     int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
+                     void *stream);
+
+/* Y[M×N] = X[M×K] · dequant(Wq)ᵀ with the weight expanded inside the kernel.
+ *   fmt : MQ_Q4_K, MQ_Q6_K or MQ_Q8_0; K a multiple of its block.
+ *   wq  : device, 16-byte aligned, N·mq_row_bytes(fmt, K) bytes.
+ *   other arguments as mq_gemm_f16cache (ws sized with fmt).
+ * The expanded f16 values are bit-identical to mq_dequant_to_f16's (minfer
+ * 05 · 8p §3.3: same rounding path), so with the same X the two paths compute
+ * the same product of the same operands. */
+int mq_gemm_fused(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y, int ldy,
+                  int M, int N, int K, void *ws, size_t ws_bytes, int split_k, void *stream);
+
+/* Static text for a return code (never NULL). */
+const char *mq_strerror(int code);
+
+/* Raw hipError_t of the last MQ_ERR_HIP returned on this thread (0 if none). */
+int mq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQ_H */

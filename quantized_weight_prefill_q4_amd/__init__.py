@@ -1,0 +1,44 @@
+"""Prefill matmul over GGUF block-quantized weights (Q4_K, Q6_K, Q8_0) for AMD
+MI355X: a load-time f16 cache with an MFMA GEMM, and a fused dequant-in-GEMM.
+
+The computation lives in the HIP library ``libmq.so`` (C ABI in
+``include/mq.h``); this package only marshals torch tensors into it.
+"""
+
+from ._lib import (
+    LIB_PATH,
+    MQ_Q4_K,
+    MQ_Q6_K,
+    MQ_Q8_0,
+    MQError,
+    lib,
+)
+from .api import (
+    FORMATS,
+    block_bytes,
+    block_elems,
+    cache_ld,
+    dequant_to_f16,
+    gemm_f16cache,
+    gemm_fused,
+    row_bytes,
+    workspace_bytes,
+)
+
+__all__ = [
+    "FORMATS",
+    "LIB_PATH",
+    "MQ_Q4_K",
+    "MQ_Q6_K",
+    "MQ_Q8_0",
+    "MQError",
+    "block_bytes",
+    "block_elems",
+    "cache_ld",
+    "dequant_to_f16",
+    "gemm_f16cache",
+    "gemm_fused",
+    "lib",
+    "row_bytes",
+    "workspace_bytes",
+]

@@ -1,0 +1,137 @@
+"""Torch-tensor front end of libmq (argument marshalling only).
+
+Each function takes device tensors, allocates its outputs (and the split-K
+workspace) with torch on the tensors' device, and calls the C ABI on torch's
+current stream.  Every step of the computation runs in the HIP library; these
+wrappers only check dtypes/devices/strides and pass pointers.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import MQ_Q4_K, MQ_Q6_K, MQ_Q8_0, check, lib
+
+FORMATS = {"q8_0": MQ_Q8_0, "q4_k": MQ_Q4_K, "q6_k": MQ_Q6_K}
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        return FORMATS[fmt.lower()]
+    return int(fmt)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need_cuda(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _row_major_2d(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def block_elems(fmt) -> int:
+    return check(lib().mq_block_elems(_fmt(fmt)), "mq_block_elems")
+
+
+def block_bytes(fmt) -> int:
+    return check(lib().mq_block_bytes(_fmt(fmt)), "mq_block_bytes")
+
+
+def row_bytes(fmt, K: int) -> int:
+    return check(lib().mq_row_bytes(_fmt(fmt), K), "mq_row_bytes")
+
+
+def cache_ld(K: int) -> int:
+    return check(lib().mq_f16cache_ld(K), "mq_f16cache_ld")
+
+
+def workspace_bytes(fmt, M: int, N: int, K: int, split_k: int = 0) -> int:
+    f = 0 if fmt in (0, None, "f16") else _fmt(fmt)
+    return check(lib().mq_gemm_workspace_bytes(f, M, N, K, split_k), "mq_gemm_workspace_bytes")
+
+
+def dequant_to_f16(wq: torch.Tensor, fmt, N: int, K: int, pad: bool = True,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode a quantized N×K weight (uint8, rows contiguous) into an f16 cache
+    [N, ld]; ld = cache_ld(K) when pad else K.  Use ``[:, :K]`` for the matrix."""
+    f = _fmt(fmt)
+    _need_cuda(wq, "wq", torch.uint8)
+    if not wq.is_contiguous():
+        raise ValueError("wq must be contiguous")
+    ld = cache_ld(K) if pad else K
+    if out is None:
+        out = torch.empty((N, ld), dtype=torch.float16, device=wq.device)
+    else:
+        _need_cuda(out, "out", torch.float16)
+        ld = _row_major_2d(out, "out")
+    check(lib().mq_dequant_to_f16(f, wq.data_ptr(), N, K, out.data_ptr(), ld, _stream(wq)),
+          "mq_dequant_to_f16")
+    return out
+
+
+def _workspace(fmt_code: int, M: int, N: int, K: int, split_k: int, device) -> torch.Tensor | None:
+    nbytes = check(lib().mq_gemm_workspace_bytes(fmt_code, M, N, K, split_k),
+                   "mq_gemm_workspace_bytes")
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+
+
+def gemm_f16cache(x: torch.Tensor, w16: torch.Tensor, K: int | None = None, split_k: int = 0,
+                  out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] (f32) = x[:, :K] @ w16[:, :K]^T with x f16 [M, >=K], w16 the f16 cache [N, ld]."""
+    _need_cuda(x, "x", torch.float16)
+    _need_cuda(w16, "w16", torch.float16)
+    ldx = _row_major_2d(x, "x")
+    ldw = _row_major_2d(w16, "w16")
+    M, N = x.shape[0], w16.shape[0]
+    K = x.shape[1] if K is None else K
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    else:
+        _need_cuda(out, "out", torch.float32)
+    ldy = _row_major_2d(out, "out")
+    if ws is None:
+        ws = _workspace(0, M, N, K, split_k, x.device)
+    check(lib().mq_gemm_f16cache(x.data_ptr(), ldx, w16.data_ptr(), ldw, out.data_ptr(), ldy,
+                                 M, N, K, 0 if ws is None else ws.data_ptr(),
+                                 0 if ws is None else ws.numel() * ws.element_size(),
+                                 split_k, _stream(x)),
+          "mq_gemm_f16cache")
+    return out
+
+
+def gemm_fused(x: torch.Tensor, wq: torch.Tensor, fmt, N: int, K: int | None = None,
+               split_k: int = 0, out: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] (f32) = x[:, :K] @ dequant(wq)^T, expanding the quantized weight in-kernel."""
+    f = _fmt(fmt)
+    _need_cuda(x, "x", torch.float16)
+    _need_cuda(wq, "wq", torch.uint8)
+    if not wq.is_contiguous():
+        raise ValueError("wq must be contiguous")
+    ldx = _row_major_2d(x, "x")
+    M = x.shape[0]
+    K = x.shape[1] if K is None else K
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    else:
+        _need_cuda(out, "out", torch.float32)
+    ldy = _row_major_2d(out, "out")
+    if ws is None:
+        ws = _workspace(f, M, N, K, split_k, x.device)
+    check(lib().mq_gemm_fused(f, x.data_ptr(), ldx, wq.data_ptr(), out.data_ptr(), ldy, M, N, K,
+                              0 if ws is None else ws.data_ptr(),
+                              0 if ws is None else ws.numel() * ws.element_size(),
+                              split_k, _stream(x)),
+          "mq_gemm_fused")
+    return out

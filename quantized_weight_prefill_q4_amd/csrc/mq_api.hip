@@ -1,0 +1,140 @@
+// C ABI of libmq: argument validation, launch planning, error reporting.
+// Every check happens before anything is enqueued, so a rejected call has no
+// side effect (Fucina "Eager GPU Offload Without A Compute Graph", ordering
+// section: submission failures are reported before return; faults after
+// submission surface at the host boundary).
+
+#include "mq.h"
+#include "mq_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+bool quant_fmt(int fmt) { return mq::block_elems(fmt) > 0; }
+
+int check_dims(int M, int N, int K) {
+    if (M <= 0 || N <= 0 || K <= 0 || M > MQ_MAX_DIM || N > MQ_MAX_DIM || K > MQ_MAX_K)
+        return MQ_ERR_SHAPE;
+    return MQ_OK;
+}
+
+bool ld_ok(int64_t ld, int64_t K) { return ld >= K && ld % 8 == 0 && ld <= MQ_MAX_K + 64; }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MQ_OK;
+    g_last_hip_error = (int)e;
+    return MQ_ERR_HIP;
+}
+
+// Shared checks of both GEMM entry points; fills the plan on success.
+int check_gemm(int fmt, const void *X, int ldx, const void *W, int64_t ldw_elems, const float *Y,
+               int ldy, int M, int N, int K, const void *ws, size_t ws_bytes, int split_k,
+               mq::GemmPlan *plan) {
+    if (!X || !W || !Y) return MQ_ERR_NULL;
+    if (fmt != mq::kFmtF16 && !quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    if (int rc = check_dims(M, N, K)) return rc;
+    const int step = fmt == mq::kFmtF16 ? 8 : mq::block_elems(fmt);
+    if (K % step) return MQ_ERR_SHAPE;
+    if (!ld_ok(ldx, K) || ldy < N) return MQ_ERR_LD;
+    if (fmt == mq::kFmtF16 && !ld_ok(ldw_elems, K)) return MQ_ERR_LD;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return MQ_ERR_ALIGN;
+    if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
+    if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
+    *plan = mq::plan_gemm(fmt, M, N, K, split_k);
+    if (plan->ws_bytes > 0 &&
+        (!ws || !aligned16(ws) || ws_bytes < (size_t)plan->ws_bytes))
+        return MQ_ERR_WORKSPACE;
+    return MQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mq_block_elems(int fmt) {
+    const int v = mq::block_elems(fmt);
+    return v < 0 ? MQ_ERR_FORMAT : v;
+}
+
+int mq_block_bytes(int fmt) {
+    const int v = mq::block_bytes(fmt);
+    return v < 0 ? MQ_ERR_FORMAT : v;
+}
+
+int64_t mq_row_bytes(int fmt, int64_t K) {
+    const int be = mq::block_elems(fmt);
+    if (be < 0) return MQ_ERR_FORMAT;
+    if (K <= 0 || K > MQ_MAX_K || K % be) return MQ_ERR_SHAPE;
+    return K / be * mq::block_bytes(fmt);
+}
+
+int64_t mq_f16cache_ld(int64_t K) {
+    if (K <= 0 || K > MQ_MAX_K) return MQ_ERR_SHAPE;
+    return (2 * K) % 2048 == 0 ? K + 64 : K;
+}
+
+int mq_dequant_to_f16(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
+                      void *stream) {
+    if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    if (!wq || !w16) return MQ_ERR_NULL;
+    if (check_dims(1, N, K) || K % mq::block_elems(fmt)) return MQ_ERR_SHAPE;
+    if (!ld_ok(ld, K)) return MQ_ERR_LD;
+    if (!aligned16(wq) || !aligned16(w16)) return MQ_ERR_ALIGN;
+    if ((int64_t)N * ld / 8 >= ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
+    return hip_status(mq::launch_dequant(fmt, wq, N, K, w16, ld, (hipStream_t)stream));
+}
+
+int64_t mq_gemm_workspace_bytes(int fmt, int M, int N, int K, int split_k) {
+    if (fmt != mq::kFmtF16 && !quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    if (int rc = check_dims(M, N, K)) return rc;
+    if (K % (fmt == mq::kFmtF16 ? 8 : mq::block_elems(fmt))) return MQ_ERR_SHAPE;
+    if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
+    if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
+    return mq::plan_gemm(fmt, M, N, K, split_k).ws_bytes;
+}
+
+int mq_gemm_f16cache(const uint16_t *X, int ldx, const uint16_t *W16, int ldw, float *Y,
+                     int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
+                     void *stream) {
+    mq::GemmPlan plan;
+    if (int rc = check_gemm(mq::kFmtF16, X, ldx, W16, ldw, Y, ldy, M, N, K, ws, ws_bytes,
+                            split_k, &plan))
+        return rc;
+    return hip_status(mq::launch_gemm(mq::kFmtF16, X, ldx, W16, ldw, Y, ldy, M, N, K, plan,
+                                      (float *)ws, (hipStream_t)stream));
+}
+
+int mq_gemm_fused(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y, int ldy,
+                  int M, int N, int K, void *ws, size_t ws_bytes, int split_k, void *stream) {
+    if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    mq::GemmPlan plan;
+    if (int rc = check_gemm(fmt, X, ldx, wq, 0, Y, ldy, M, N, K, ws, ws_bytes, split_k, &plan))
+        return rc;
+    const int64_t row_bytes = (int64_t)K / mq::block_elems(fmt) * mq::block_bytes(fmt);
+    return hip_status(mq::launch_gemm(fmt, X, ldx, wq, row_bytes, Y, ldy, M, N, K, plan,
+                                      (float *)ws, (hipStream_t)stream));
+}
+
+const char *mq_strerror(int code) {
+    switch (code) {
+    case MQ_OK: return "success";
+    case MQ_ERR_NULL: return "a required pointer is NULL";
+    case MQ_ERR_FORMAT: return "unknown weight format";
+    case MQ_ERR_SHAPE: return "M, N or K out of range, or K not a multiple of the block size";
+    case MQ_ERR_LD: return "a leading dimension is too small, too large or not a multiple of 8";
+    case MQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MQ_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than required";
+    case MQ_ERR_SPLIT: return "split_k out of range for this problem";
+    case MQ_ERR_HIP: return "the HIP runtime rejected a launch";
+    default: return "unknown error code";
+    }
+}
+
+int mq_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Host-side interface between the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kFmtF16 = 0;  // the f16-cache operand of the GEMM
+constexpr int kFmtQ8_0 = 8;
+constexpr int kFmtQ4_K = 12;
+constexpr int kFmtQ6_K = 14;
+
+inline int block_elems(int fmt) {
+    return fmt == kFmtQ8_0 ? 32 : (fmt == kFmtQ4_K || fmt == kFmtQ6_K) ? 256 : -1;
+}
+inline int block_bytes(int fmt) {
+    return fmt == kFmtQ8_0 ? 34 : fmt == kFmtQ4_K ? 144 : fmt == kFmtQ6_K ? 210 : -1;
+}
+
+// Decode launcher (arguments already validated).
+hipError_t launch_dequant(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
+                          hipStream_t stream);
+
+// Launch shape of one GEMM: tile sizes, K split and workspace.
+struct GemmPlan {
+    int bm, bn;             // block tile (M rows of X, N rows of W)
+    int tiles_m, tiles_n;
+    int k_steps;            // ceil(K / 64)
+    int split;              // number of K partitions actually launched (>= 1)
+    int steps_per_split;    // k-steps per partition
+    int64_t ws_bytes;       // split > 1: split * M * N * 4, else 0
+};
+
+// split_req: 0 = choose, 1..16 = requested partitions (clamped to the k-steps).
+GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req);
+
+// Launch the GEMM (and the split-K reduction when plan.split > 1).
+//   W    : uint16 f16 cache when fmt == kFmtF16, else quantized bytes.
+//   ldw  : f16 row stride (elements) or quantized row bytes.
+hipError_t launch_gemm(int fmt, const uint16_t *X, int ldx, const void *W, int64_t ldw,
+                       float *Y, int ldy, int M, int N, int K, const GemmPlan &plan, float *ws,
+                       hipStream_t stream);
+
+}  // namespace mq

@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/mq.h declares, agrees with the binding's signatures, and rejects
+invalid arguments before launching anything (every call below has at least one
+invalid argument, so no HIP call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_weight_prefill_q4_amd as mq
+from quantized_weight_prefill_q4_amd import _lib
+from oracle import cache_ld as oracle_ld, row_bytes as oracle_row_bytes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mq.h")
+FAKE = 0x100000   # a 16-byte-aligned address that is never dereferenced
+MIS = FAKE + 2    # misaligned
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(mq_\w+)\s*\(([^)]*)\)\s*;", text):
+        args = [a for a in m.group(2).split(",") if a.strip() and a.strip() != "void"]
+        out[m.group(1)] = len(args)
+    return out
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_header_symbols_exported_and_bound(L):
+    decl = _declared()
+    assert set(decl) == set(_lib.SIGNATURES), "binding and header disagree"
+    for name, nargs in decl.items():
+        assert hasattr(L, name), f"{name} not exported"
+        assert len(_lib.SIGNATURES[name][1]) == nargs, name
+
+
+def test_format_tables(L):
+    assert (L.mq_block_elems(12), L.mq_block_bytes(12)) == (256, 144)
+    assert (L.mq_block_elems(14), L.mq_block_bytes(14)) == (256, 210)
+    assert (L.mq_block_elems(8), L.mq_block_bytes(8)) == (32, 34)
+    assert L.mq_block_elems(2) == _lib.MQ_ERR_FORMAT
+    for fmt, K in ((12, 3584), (14, 18944), (8, 4096), (12, 256), (8, 32)):
+        assert L.mq_row_bytes(fmt, K) == oracle_row_bytes(fmt, K)
+    assert L.mq_row_bytes(12, 100) == _lib.MQ_ERR_SHAPE
+    assert L.mq_row_bytes(99, 256) == _lib.MQ_ERR_FORMAT
+
+
+@pytest.mark.parametrize("K", [8, 256, 512, 1024, 3584, 4096, 14336, 18944, 2048, 3072])
+def test_cache_ld_matches_oracle(L, K):
+    assert L.mq_f16cache_ld(K) == oracle_ld(K)
+
+
+def test_dequant_rejects(L):
+    d = L.mq_dequant_to_f16
+    assert d(5, FAKE, 4, 256, FAKE, 256, None) == _lib.MQ_ERR_FORMAT
+    assert d(12, None, 4, 256, FAKE, 256, None) == _lib.MQ_ERR_NULL
+    assert d(12, FAKE, 4, 256, None, 256, None) == _lib.MQ_ERR_NULL
+    assert d(12, FAKE, 0, 256, FAKE, 256, None) == _lib.MQ_ERR_SHAPE
+    assert d(12, FAKE, 4, 100, FAKE, 104, None) == _lib.MQ_ERR_SHAPE
+    assert d(8, FAKE, 4, 48, FAKE, 48, None) == _lib.MQ_ERR_SHAPE
+    assert d(12, FAKE, 4, 256, FAKE, 255, None) == _lib.MQ_ERR_LD
+    assert d(12, FAKE, 4, 256, FAKE, 260, None) == _lib.MQ_ERR_LD
+    assert d(12, MIS, 4, 256, FAKE, 256, None) == _lib.MQ_ERR_ALIGN
+    assert d(12, FAKE, 4, 256, MIS, 256, None) == _lib.MQ_ERR_ALIGN
+
+
+def test_gemm_rejects(L):
+    g = L.mq_gemm_f16cache
+    ok = dict(X=FAKE, ldx=512, W=FAKE, ldw=512, Y=FAKE, ldy=256, M=64, N=256, K=512,
+              ws=None, wsb=0, split=1, s=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return g(a["X"], a["ldx"], a["W"], a["ldw"], a["Y"], a["ldy"], a["M"], a["N"], a["K"],
+                 a["ws"], a["wsb"], a["split"], a["s"])
+
+    # each call carries exactly one defect
+    assert call(X=None) == _lib.MQ_ERR_NULL
+    assert call(Y=None) == _lib.MQ_ERR_NULL
+    assert call(M=0) == _lib.MQ_ERR_SHAPE
+    assert call(N=-1) == _lib.MQ_ERR_SHAPE
+    assert call(K=100, ldx=104, ldw=104) == _lib.MQ_ERR_SHAPE
+    assert call(ldx=500) == _lib.MQ_ERR_LD
+    assert call(ldw=520 + 4) == _lib.MQ_ERR_LD
+    assert call(ldy=255) == _lib.MQ_ERR_LD
+    assert call(X=MIS) == _lib.MQ_ERR_ALIGN
+    assert call(W=MIS) == _lib.MQ_ERR_ALIGN
+    assert call(split=17) == _lib.MQ_ERR_SPLIT
+    assert call(split=-1) == _lib.MQ_ERR_SPLIT
+    # forced split without workspace
+    assert call(split=4) == _lib.MQ_ERR_WORKSPACE
+    need = L.mq_gemm_workspace_bytes(0, 64, 256, 512, 4)
+    assert need == 4 * 64 * 256 * 4
+    assert call(split=4, ws=FAKE, wsb=need - 1) == _lib.MQ_ERR_WORKSPACE
+    assert call(split=4, ws=MIS, wsb=need) == _lib.MQ_ERR_WORKSPACE
+
+
+def test_fused_rejects(L):
+    f = L.mq_gemm_fused
+    assert f(5, FAKE, 512, FAKE, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_FORMAT
+    assert f(0, FAKE, 512, FAKE, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_FORMAT
+    assert f(12, FAKE, 512, None, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_NULL
+    assert f(12, FAKE, 512, FAKE, FAKE, 256, 64, 256, 480, None, 0, 1, None) == _lib.MQ_ERR_SHAPE
+    assert f(8, FAKE, 64, FAKE, FAKE, 256, 64, 256, 48, None, 0, 1, None) == _lib.MQ_ERR_SHAPE
+    assert f(12, FAKE, 512, MIS, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_ALIGN
+    assert f(12, FAKE, 512, FAKE, FAKE, 256, 64, 256, 512, None, 0, 4, None) == _lib.MQ_ERR_WORKSPACE
+
+
+def test_workspace_planning(L):
+    # k/v projection at M=2048 underfills 256 CUs with 256x128 tiles -> split
+    ws = L.mq_gemm_workspace_bytes(12, 2048, 512, 3584, 0)
+    assert ws > 0 and ws % (2048 * 512 * 4) == 0
+    assert L.mq_gemm_workspace_bytes(0, 2048, 512, 3584, 0) == ws
+    # gate/up fill the machine -> no split
+    assert L.mq_gemm_workspace_bytes(0, 2048, 18944, 3584, 0) == 0
+    assert L.mq_gemm_workspace_bytes(0, 64, 512, 512, 1) == 0
+    # forced splits are clamped to the number of 64-wide k-steps
+    assert L.mq_gemm_workspace_bytes(0, 64, 128, 128, 16) == 2 * 64 * 128 * 4
+    assert L.mq_gemm_workspace_bytes(99, 64, 128, 128, 1) == _lib.MQ_ERR_FORMAT
+
+
+def test_strerror_total(L):
+    for code in range(-9, 1):
+        assert isinstance(L.mq_strerror(code), bytes)
+    assert L.mq_last_hip_error() == 0
+
+
+def test_binding_errors_are_raised():
+    with pytest.raises(mq.MQError) as e:
+        _lib.check(_lib.MQ_ERR_LD, "x")
+    assert e.value.code == _lib.MQ_ERR_LD
+    assert mq.cache_ld(4096) == 4160 and mq.row_bytes("q6_k", 18944) == 15540

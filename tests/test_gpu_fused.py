@@ -1,0 +1,114 @@
+"""Parity of mq_gemm_fused (dequant inside the GEMM) with the oracle and with
+the cache path.
+
+* one-hot activations: Y = dequant(W)ᵀ exactly, so the in-kernel expansion is
+  checked bit for bit against the oracle's decode (by value; ±0 compare equal);
+* integer-mode weights and activations: exact;
+* random inputs: within tolerance of the f64 oracle, and bit-identical to the
+  f16-cache GEMM on the device-built cache (same tiles, same k order, same f16
+  operands — the invariant that the two shapes of the method agree);
+* the Llama-3.1-8B-like sweep shapes at M = 128 and 2048 on sampled rows."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import announce, check_gemm, needs_gpu, to_dev_f16, to_dev_u8, to_host
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+import quantized_weight_prefill_q4_amd as mq  # noqa: E402
+
+FMT_NAME = {12: "Q4_K", 14: "Q6_K", 8: "Q8_0"}
+
+
+def _fused(fmt, x_bits, q, N, K, split_k=0):
+    announce("gemm_fused", FMT_NAME[fmt], f"M={x_bits.shape[0]}", f"N={N}", f"K={K}",
+             f"split={split_k}")
+    return mq.gemm_fused(to_dev_f16(x_bits), to_dev_u8(q), fmt, N, K, split_k=split_k)
+
+
+@pytest.mark.parametrize("fmt,N,K", [(12, 300, 256), (12, 128, 512), (14, 200, 256),
+                                     (14, 130, 512), (8, 257, 96), (8, 64, 512), (8, 100, 32)])
+def test_onehot_expansion_is_the_decode(fmt, N, K):
+    q = synth.weights(fmt, synth.rng(30, 0, fmt, N), N, K)
+    x = synth.activations(None, K, K, mode="onehot")
+    Y = to_host(_fused(fmt, x, q, N, K))
+    exp = oracle.dequant_ref(fmt, q, N, K).view(np.float16).astype(np.float32).T
+    assert np.array_equal(Y, exp)
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(12, 100, 300, 1024), (14, 70, 130, 2048),
+                                       (8, 33, 257, 1056)])
+@pytest.mark.parametrize("split", [0, 1, 3])
+def test_integer_exact(fmt, M, N, K, split):
+    q = synth.weights(fmt, synth.rng(31, 0, fmt, 0), N, K, mode="integer")
+    x = synth.activations(synth.rng(31, role=1), M, K, mode="integer")
+    Y = to_host(_fused(fmt, x, q, N, K, split_k=split))
+    Yref, _ = oracle.gemm_ref(x, oracle.dequant_ref(fmt, q, N, K))
+    assert np.array_equal(Y.astype(np.float64), Yref)
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(12, 64, 512, 512), (12, 129, 200, 1280),
+                                       (14, 257, 96, 768), (8, 65, 333, 4128),
+                                       (8, 1, 1, 32), (14, 1, 3, 256)])
+def test_random_tolerance_and_cache_identity(fmt, M, N, K):
+    q = synth.weights(fmt, synth.rng(32, 0, fmt, M), N, K)
+    x = synth.activations(synth.rng(32, role=1), M, K)
+    Yf = to_host(_fused(fmt, x, q, N, K))
+    w16 = oracle.dequant_ref(fmt, q, N, K)
+    check_gemm(Yf, x, w16, K, f"fused {FMT_NAME[fmt]} {M}x{N}x{K}")
+    announce("dequant+gemm_f16cache", FMT_NAME[fmt], f"M={M} N={N} K={K}")
+    cache = mq.dequant_to_f16(to_dev_u8(q), fmt, N, K)
+    Yc = to_host(mq.gemm_f16cache(to_dev_f16(x), cache, K))
+    assert np.array_equal(Yf, Yc), f"fused and cache paths differ: max {np.abs(Yf - Yc).max()}"
+
+
+SWEEP = [("Q4_K 4096^2", 12, 4096, 4096), ("Q4_K 14336x4096", 12, 14336, 4096),
+         ("Q4_K 4096x14336", 12, 4096, 14336), ("Q8_0 4096^2", 8, 4096, 4096),
+         ("Q6_K 3584x18944", 14, 3584, 18944)]
+
+
+@pytest.mark.parametrize("M", [128, 2048])
+@pytest.mark.parametrize("name,fmt,N,K", SWEEP)
+def test_sweep_shapes(name, fmt, N, K, M):
+    q = synth.weights(fmt, synth.rng(33, 0, fmt, N % 1000), N, K)
+    x = synth.activations(synth.rng(33, role=1), M, K)
+    Yf = to_host(_fused(fmt, x, q, N, K))
+    announce("dequant+gemm_f16cache", name, f"M={M}")
+    cache = mq.dequant_to_f16(to_dev_u8(q), fmt, N, K)
+    Yc = to_host(mq.gemm_f16cache(to_dev_f16(x), cache, K))
+    assert np.array_equal(Yf, Yc)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(M, 16)]))
+    check_gemm(Yf[rows], x, oracle.dequant_ref(fmt, q, N, K), K, name, rows=rows)
+
+
+def test_fused_expands_golden_blocks():
+    """The hand-derived Q4_K blocks (worked vector, f32-then-f16 double rounding)
+    expanded inside the GEMM: one-hot X makes Y the expanded weights."""
+    from conftest import read_golden
+    from oracle.encode import pack_q4k
+
+    g = read_golden("q4k_worked.txt")
+    qs = [(i % 16) | ((15 - i % 16) << 4) for i in range(128)]
+    q = []
+    for e in range(256):
+        c, r = divmod(e, 64)
+        b = qs[32 * c + r % 32]
+        q.append(b & 15 if r < 32 else b >> 4)
+    row0 = pack_q4k(0x3C00, 0x3800, [int(t) for t in g["scales"][0].split()],
+                    [int(t) for t in g["mins"][0].split()], q)
+    gd = read_golden("q4k_double_rounding.txt")
+    qd = [0] * 256
+    qd[0] = int(gd["q0"][0])
+    row1 = pack_q4k(int(gd["d_bits"][0], 16), int(gd["dmin_bits"][0], 16),
+                    [int(t) for t in gd["scales"][0].split()],
+                    [int(t) for t in gd["mins"][0].split()], qd)
+    wq = np.frombuffer(row0 + row1, np.uint8).copy()
+    x = synth.activations(None, 256, 256, mode="onehot")
+    Y = to_host(_fused(12, x, wq, 2, 256))
+    for tok in g["expect"][0].split():
+        e, v = tok.split(":")
+        assert Y[int(e), 0] == float(v), tok
+    assert np.float16(Y[0, 1]).view(np.uint16) == 0x3C02
