@@ -1,0 +1,375 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-weight prefill matmul on one MI355X.
+
+Workload (the timed step): one prefill forward's matmuls over a full 28-layer
+7B weight set — per layer q, o (3584×3584), k, v (512×3584), gate, up
+(18944×3584) in Q4_K and down (3584×18944) in Q6_K — at M = 2048 tokens with
+f16 N(0,1) activations, 196 GEMMs Y = X·Wᵀ on the persistent f16 cache.
+Before the steps, the load phase decodes all 196 weights into the cache
+(the method's one-time dequant; timed, reported as GB/s).  After them, the
+fused dequant-in-GEMM is timed on the same forward, and the fused-vs-cache
+crossover in M is swept on Llama-3.1-8B-like shapes.
+
+Inputs are synthetic and seeded (the pages' real GGUF models are not
+available): the 4.2 GB weight set is drawn on the device with torch's seeded
+generator, same distributions as the numpy generator the tests use.
+
+Prints human-readable tables on stderr and ONE JSON line on stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "prefill GEMM TFLOP/s + matmul tok/s (7B Q4_K, M=2048); dequant GB/s"
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense f16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+ROOFLINE_KERNEL = "gemm_kernel<256, 128, f16 cache, full-K>"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--M", type=int, default=2048)
+    p.add_argument("--layers", type=int, default=synth.N_LAYERS_7B)
+    p.add_argument("--load-reps", type=int, default=3)
+    p.add_argument("--fused-steps", type=int, default=5)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=128,
+                   help="token rows of the oracle sample (one layer's 7 matrices)")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# GPU phases
+# ---------------------------------------------------------------------------
+
+def make_weights(torch, mq, layers, dev):
+    """Quantized weights on the device plus their (empty) f16 caches."""
+    W = []
+    for L in range(layers):
+        row = {}
+        for mi, (name, fmt, N, K) in enumerate(synth.LAYER_7B):
+            q = synth.weights_device(fmt, 1000 * L + mi, N, K, dev)
+            cache = torch.empty((N, mq.cache_ld(K)), dtype=torch.float16, device=dev)
+            row[name] = (fmt, N, K, q, cache)
+        W.append(row)
+    torch.cuda.synchronize()
+    return W
+
+
+def load_phase(torch, mq, W, reps):
+    """Decode every weight into its cache; per-call HIP-event times (ms)."""
+    best = None
+    for _ in range(reps):
+        evs = []
+        for row in W:
+            for name, (fmt, N, K, q, cache) in row.items():
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                mq.dequant_to_f16(q, fmt, N, K, out=cache)
+                b.record()
+                evs.append((name, fmt, N, K, q.numel(), a, b))
+        torch.cuda.synchronize()
+        rec = [(name, fmt, N, K, qb, a.elapsed_time(b)) for name, fmt, N, K, qb, a, b in evs]
+        tot = sum(r[-1] for r in rec)
+        if best is None or tot < best[0]:
+            best = (tot, rec)
+    return best[1]
+
+
+def forward(mq, W, xa, xf, ys, ws, events=None):
+    """One prefill forward: 196 cache GEMMs (events[i] recorded before call i)."""
+    i = 0
+    for row in W:
+        for name, (fmt, N, K, q, cache) in row.items():
+            if events is not None:
+                events[i].record()
+            mq.gemm_f16cache(xf if name == "down" else xa, cache, K, out=ys[name], ws=ws)
+            i += 1
+    if events is not None:
+        events[i].record()
+
+
+def forward_fused(mq, W, xa, xf, ys, ws):
+    for row in W:
+        for name, (fmt, N, K, q, cache) in row.items():
+            mq.gemm_fused(xf if name == "down" else xa, q, fmt, N, K, out=ys[name], ws=ws)
+
+
+def sweep(torch, mq, dev, log_rows):
+    """Fused vs cache GEMM time per (shape, M); rotates weight copies over > 512 MB."""
+    out = {}
+    for si, (name, fmt, N, K) in enumerate(synth.SWEEP_8B):
+        q0 = synth.weights_device(fmt, 5000 + si, N, K, dev)
+        cache0 = mq.dequant_to_f16(q0, fmt, N, K)
+        nc = max(3, -(-512 * 2 ** 20 // (cache0.numel() * 2)))
+        nq = max(3, -(-512 * 2 ** 20 // q0.numel()))
+        caches = [cache0] + [cache0.clone() for _ in range(nc - 1)]
+        qs = [q0] + [q0.clone() for _ in range(nq - 1)]
+        x = synth.activations_device(6000 + si, max(synth.SWEEP_M), K, dev)
+        res = {}
+        for M in synth.SWEEP_M:
+            xm = x[:M]
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            ws_c = torch.empty(max(1, mq.workspace_bytes(0, M, N, K) // 4), dtype=torch.float32, device=dev)
+            ws_f = torch.empty(max(1, mq.workspace_bytes(fmt, M, N, K) // 4), dtype=torch.float32, device=dev)
+            t = {}
+            for path in ("cache", "fused"):
+                reps = 12
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+                for r in range(reps + 2):                  # 2 warm-up calls
+                    if r >= 2:
+                        evs[r - 2].record()
+                    if path == "cache":
+                        mq.gemm_f16cache(xm, caches[r % nc], K, out=y, ws=ws_c)
+                    else:
+                        mq.gemm_fused(xm, qs[r % nq], fmt, N, K, out=y, ws=ws_f)
+                evs[reps].record()
+                torch.cuda.synchronize()
+                d = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(reps)]
+                t[path] = statistics.median(d)
+            flops = 2.0 * M * N * K
+            res[M] = {"cache_us": round(t["cache"], 2), "fused_us": round(t["fused"], 2),
+                      "cache_tflops": round(flops / t["cache"] / 1e6, 1),
+                      "fused_tflops": round(flops / t["fused"] / 1e6, 1)}
+            log_rows.append(f"  {name:16s} M={M:5d}  cache {t['cache']:9.1f} us ({res[M]['cache_tflops']:7.1f} TF/s)"
+                            f"  fused {t['fused']:9.1f} us ({res[M]['fused_tflops']:7.1f} TF/s)")
+        wins = [M for M in synth.SWEEP_M if res[M]["cache_us"] < res[M]["fused_us"]]
+        if not wins:
+            cross = f">{max(synth.SWEEP_M)}"
+        elif wins[0] == min(synth.SWEEP_M):
+            cross = f"<={min(synth.SWEEP_M)}"
+        else:
+            cross = str(wins[0])
+        out[name] = {"crossover_M": cross, "by_M": res}
+        del caches, qs, cache0, q0
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(rows: int):
+    import oracle
+
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) \
+            if threadpoolctl.threadpool_info() else 1
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t_deq = t_gemm = 0.0
+    deq_bytes = 0
+    for mi, (name, fmt, N, K) in enumerate(synth.LAYER_7B):
+        q = synth.weights(fmt, synth.rng(5, 0, mi, 0), N, K)
+        x = synth.activations(synth.rng(5, 0, mi, 1), rows, K)
+        t0 = time.perf_counter()
+        w16 = oracle.dequant_ref(fmt, q, N, K)
+        t1 = time.perf_counter()
+        oracle.gemm_ref(x, w16, K)
+        t2 = time.perf_counter()
+        t_deq += t1 - t0
+        t_gemm += t2 - t1
+        deq_bytes += q.nbytes + 2 * N * K
+    layers = synth.N_LAYERS_7B
+    return {
+        "value": round(rows / (t_gemm * layers), 2),
+        "unit": "tok/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"1 of {layers} layers (its 7 matrices), {rows} of 2048 token rows; "
+                   f"f64 oracle gemm_ref (Y and S); tok/s = rows / (layer time x {layers})"),
+        "gemm_layer_s": round(t_gemm, 3),
+        "dequant_gbs": round(deq_bytes / t_deq / 1e9, 3),
+        "dequant_layer_s": round(t_deq, 3),
+    }
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the matmul path runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_weight_prefill_q4_amd as mq
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, layers = args.M, args.layers
+    log(f"[bench] device {torch.cuda.get_device_name(0)}, library {mq.LIB_PATH}")
+
+    # -- weights and the load phase (one-time dequant into the f16 cache) ------
+    t0 = time.time()
+    W = make_weights(torch, mq, layers, dev)
+    qbytes = sum(r[n][3].numel() for r in W for n in r)
+    cbytes = sum(r[n][1] * r[n][2] * 2 for r in W for n in r)
+    log(f"[bench] {layers * 7} weights drawn on device in {time.time() - t0:.1f}s: "
+        f"{qbytes / 1e9:.3f} GB quantized, {cbytes / 1e9:.3f} GB f16")
+    rec = load_phase(torch, mq, W, args.load_reps)
+    deq_ms = sum(r[-1] for r in rec)
+    deq_gbs = (qbytes + cbytes) / (deq_ms / 1e3) / 1e9
+    per_fmt = {}
+    for name, fmt, N, K, qb, ms in rec:
+        f = per_fmt.setdefault("Q6_K" if fmt == 14 else "Q4_K", [0, 0.0])
+        f[0] += qb + 2 * N * K
+        f[1] += ms
+    log(f"[bench] load phase: {deq_ms:.2f} ms for {len(rec)} dequants, {deq_gbs:.0f} GB/s "
+        f"({100 * deq_gbs / PEAK_HBM_GBS:.1f}% of HBM peak); " +
+        ", ".join(f"{k} {v[0] / v[1] / 1e6:.0f} GB/s" for k, v in per_fmt.items()))
+
+    # -- the timed forward --------------------------------------------------------
+    xa = synth.activations_device(7001, M, 3584, dev)
+    xf = synth.activations_device(7002, M, 18944, dev)
+    ys = {n: torch.empty((M, N), dtype=torch.float32, device=dev) for n, _, N, _ in synth.LAYER_7B}
+    ws_bytes = max(mq.workspace_bytes(0, M, N, K) for _, _, N, K in synth.LAYER_7B)
+    ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device=dev)
+    calls = [(n, f, N, K) for row in W for n, (f, N, K, _, _) in row.items()]
+
+    for _ in range(args.warmup):
+        forward(mq, W, xa, xf, ys, ws)
+    steps_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+                    for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        forward(mq, W, xa, xf, ys, ws, events=steps_events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    ev_step_ms = statistics.median(e[0].elapsed_time(e[-1]) for e in steps_events)
+
+    # per-call durations (median over steps), per shape and for the roofline kernel
+    per_call = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(calls))]
+                         for e in steps_events])
+    med_call = np.median(per_call, axis=0)
+    flops = np.array([2.0 * M * N * K for _, _, N, K in calls])
+    shape_rows, full_k = [], []
+    for n, f, N, K in synth.LAYER_7B:
+        idx = [i for i, c in enumerate(calls) if c[0] == n]
+        t_us = float(med_call[idx].mean() * 1e3)
+        shape_rows.append((n, N, K, t_us, 2.0 * M * N * K / t_us / 1e6))
+        if mq.workspace_bytes(0, M, N, K) == 0:
+            full_k += idx
+    full_k = np.array(sorted(full_k))
+    ach = float(flops[full_k].sum() / (per_call[:, full_k].sum(axis=1).mean() / 1e3) / 1e12)
+    avg_launch_us = float(per_call[:, full_k].mean() * 1e3)
+    gemm_tflops = float(flops.sum() / (ev_step_ms / 1e3) / 1e12)
+    tok_s = M * args.steps / wall
+    log(f"[bench] forward: {ms_per_step:.3f} ms/step wall, {ev_step_ms:.3f} ms in events, "
+        f"{tok_s:.0f} matmul tok/s, {gemm_tflops:.0f} TFLOP/s over {len(calls)} GEMMs")
+    for n, N, K, t_us, tf in shape_rows:
+        log(f"    {n:5s} {N:6d}x{K:<6d} {t_us:9.1f} us  {tf:7.1f} TFLOP/s  "
+            f"({100 * tf / PEAK_F16_TFLOPS:.1f}% of peak)")
+    log(f"[bench] roofline kernel ({ROOFLINE_KERNEL}, {len(full_k)} launches/step): "
+        f"{ach:.0f} TFLOP/s = {100 * ach / PEAK_F16_TFLOPS:.1f}% of {PEAK_F16_TFLOPS:.0f}, "
+        f"avg launch {avg_launch_us:.1f} us")
+
+    # -- fused forward (no cache) ---------------------------------------------------
+    fused = None
+    if args.fused_steps > 0:
+        forward_fused(mq, W, xa, xf, ys, ws)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.fused_steps):
+            forward_fused(mq, W, xa, xf, ys, ws)
+        b.record()
+        torch.cuda.synchronize()
+        f_ms = a.elapsed_time(b) / args.fused_steps
+        fused = {"ms_per_step": round(f_ms, 3), "tok_s": round(M / (f_ms / 1e3), 1),
+                 "tflops": round(flops.sum() / (f_ms / 1e3) / 1e12, 1)}
+        log(f"[bench] fused forward: {f_ms:.3f} ms/step, {fused['tok_s']:.0f} tok/s")
+
+    # -- crossover sweep -------------------------------------------------------------
+    cross = None
+    if not args.no_sweep:
+        del W
+        torch.cuda.empty_cache()
+        rows = []
+        cross = sweep(torch, mq, dev, rows)
+        log("[bench] fused vs cache sweep (median of 12 calls, rotating copies > 512 MB):")
+        for r in rows:
+            log(r)
+        log("  crossover M (smallest M where the cache GEMM is faster): " +
+            ", ".join(f"{k}: {v['crossover_M']}" for k, v in cross.items()))
+
+    # -- CPU oracle baseline -------------------------------------------------------------
+    cpu = None
+    if not args.no_cpu:
+        t0 = time.time()
+        cpu = cpu_baseline(args.cpu_rows)
+        log(f"[bench] cpu oracle: {cpu['value']} tok/s on {cpu['cores']} threads "
+            f"({time.time() - t0:.1f}s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("7B prefill matmuls: 28 layers x {q,o 3584x3584, k,v 512x3584, "
+                         "gate,up 18944x3584 Q4_K; down 3584x18944 Q6_K}, f16 cache, M=2048"),
+            "M": M, "layers": layers, "gemms_per_step": len(calls),
+            "quant_gb": round(qbytes / 1e9, 3), "cache_gb": round(cbytes / 1e9, 3),
+        },
+        "gemm_tflops": round(gemm_tflops, 1),
+        "dequant_gbs": round(deq_gbs, 1),
+        "dequant_ms": round(deq_ms, 3),
+        "redequant_tok_s": round(M / ((ev_step_ms + deq_ms) / 1e3), 1),
+        "per_shape_tflops": {n: round(tf, 1) for n, _, _, _, tf in shape_rows},
+        "roofline": {
+            "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": None,
+            "kernel": ROOFLINE_KERNEL, "avg_launch_us": round(avg_launch_us, 2),
+            "launches_per_step": int(len(full_k)),
+        },
+        "dequant_roofline": {
+            "bound": "hbm", "achieved": round(deq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(deq_gbs / PEAK_HBM_GBS, 4),
+        },
+        "fused": fused,
+        "crossover": cross,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

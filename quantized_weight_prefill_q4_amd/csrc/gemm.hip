@@ -359,7 +359,9 @@ template <int ROWS> struct BLoaderFor<ROWS, kFmtQ8_0> { typedef Q80Loader<ROWS> 
 // ---------------------------------------------------------------------------
 // The GEMM kernel.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int FMT>
+// PARTIAL: the launch is split along K and writes f32 partial planes (a
+// distinct symbol, so profiles tell the two launch kinds apart).
+template <int BM, int BN, int FMT, bool PARTIAL>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
     constexpr int WN = 2;
     constexpr int TM = BM / 2, TN = BN / WN;
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
 
     // C layout of a 32x32 MFMA block: lane holds column (lane & 31) and rows
     // 8·(r/4) + 4·(lane/32) + r%4 for accumulator element r.
-    float *Yp = a.Y + (int64_t)s * a.plane;
+    float *Yp = PARTIAL ? a.Y + (int64_t)s * a.plane : a.Y;
     const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -461,17 +463,20 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ w
 }
 
 template <int BM, int FMT>
-hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_kernel<BM, 128, FMT>), dim3(grid), dim3(kThreads), 0, stream, a);
+hipError_t launch_tile(const Args &a, int grid, bool partial, hipStream_t stream) {
+    if (partial)
+        hipLaunchKernelGGL((gemm_kernel<BM, 128, FMT, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BM, 128, FMT, false>), dim3(grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_fmt(const Args &a, int bm, int grid, hipStream_t stream) {
+hipError_t launch_fmt(const Args &a, int bm, int grid, bool partial, hipStream_t stream) {
     switch (bm) {
-    case 64: return launch_tile<64, FMT>(a, grid, stream);
-    case 128: return launch_tile<128, FMT>(a, grid, stream);
-    default: return launch_tile<256, FMT>(a, grid, stream);
+    case 64: return launch_tile<64, FMT>(a, grid, partial, stream);
+    case 128: return launch_tile<128, FMT>(a, grid, partial, stream);
+    default: return launch_tile<256, FMT>(a, grid, partial, stream);
     }
 }
 
@@ -529,12 +534,13 @@ hipError_t launch_gemm(int fmt, const uint16_t *X, int ldx, const void *W, int64
         a.plane = 0;
     }
     const int grid = plan.tiles_m * plan.tiles_n * plan.split;
+    const bool partial = plan.split > 1;
     hipError_t e;
     switch (fmt) {
-    case kFmtQ4_K: e = launch_fmt<kFmtQ4_K>(a, plan.bm, grid, stream); break;
-    case kFmtQ6_K: e = launch_fmt<kFmtQ6_K>(a, plan.bm, grid, stream); break;
-    case kFmtQ8_0: e = launch_fmt<kFmtQ8_0>(a, plan.bm, grid, stream); break;
-    default: e = launch_fmt<kFmtF16>(a, plan.bm, grid, stream); break;
+    case kFmtQ4_K: e = launch_fmt<kFmtQ4_K>(a, plan.bm, grid, partial, stream); break;
+    case kFmtQ6_K: e = launch_fmt<kFmtQ6_K>(a, plan.bm, grid, partial, stream); break;
+    case kFmtQ8_0: e = launch_fmt<kFmtQ8_0>(a, plan.bm, grid, partial, stream); break;
+    default: e = launch_fmt<kFmtF16>(a, plan.bm, grid, partial, stream); break;
     }
     if (e != hipSuccess || plan.split == 1) return e;
     const uint32_t total = (uint32_t)M * (uint32_t)N;

@@ -120,3 +120,52 @@ SWEEP_8B = (
     ("q80_4096x4096", Q8_0, 4096, 4096),
 )
 SWEEP_M = (128, 512, 1024, 2048)
+
+
+# ---------------------------------------------------------------------------
+# Device-side drawing of the same distributions (torch's seeded generator),
+# used where gigabytes of weights are needed quickly (the 28-layer benchmark
+# set).  Same fields and distributions as ``weights``; a different random
+# stream, so values differ from the numpy generator for the same seed.
+# ---------------------------------------------------------------------------
+
+def weights_device(fmt: int, seed: int, N: int, K: int, device, mode: str = "random"):
+    """Quantized N×K weight as a contiguous uint8 device tensor [N, row_bytes]."""
+    import torch
+
+    if K % _ELEMS[fmt]:
+        raise ValueError(f"K={K} not a multiple of {_ELEMS[fmt]}")
+    nb = K // _ELEMS[fmt]
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([SEED_BASE, seed]).generate_state(1)[0]))
+
+    def f16_abs_normal(scale):
+        z = torch.randn((N, nb), generator=g, device=device, dtype=torch.float32)
+        return (z.abs() * scale).to(torch.float16).view(torch.uint8).view(N, nb, 2)
+
+    one = torch.tensor([0x00, 0x3C], dtype=torch.uint8, device=device)
+    blk = torch.randint(0, 256, (N, nb, _BYTES[fmt]), generator=g, device=device,
+                        dtype=torch.uint8)
+    if fmt == Q4_K:
+        blk[..., 0:2] = one if mode == "integer" else f16_abs_normal(2.0 ** -7)
+        blk[..., 2:4] = one if mode == "integer" else f16_abs_normal(2.0 ** -7)
+    elif fmt == Q6_K:
+        sc = torch.randint(-32, 32, (N, nb, 16), generator=g, device=device, dtype=torch.int8)
+        blk[..., 192:208] = sc.view(torch.uint8)
+        blk[..., 208:210] = one if mode == "integer" else f16_abs_normal(2.0 ** -9)
+    elif fmt == Q8_0:
+        q = torch.randint(-127, 128, (N, nb, 32), generator=g, device=device, dtype=torch.int8)
+        blk[..., 2:34] = q.view(torch.uint8)
+        blk[..., 0:2] = one if mode == "integer" else f16_abs_normal(2.0 ** -7)
+    else:
+        raise ValueError(f"unknown format {fmt}")
+    return blk.view(N, nb * _BYTES[fmt])
+
+
+def activations_device(seed: int, M: int, K: int, device):
+    """f16 N(0,1) activations [M, K] drawn on the device."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([SEED_BASE, seed, 1]).generate_state(1)[0]))
+    return torch.randn((M, K), generator=g, device=device, dtype=torch.float32).to(torch.float16)
