@@ -62,38 +62,62 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
     return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One buffer_load_dwordx4 ... lds: 16 bytes at `voff` of `rs` for every lane,
+// landing at LDS byte address `lds` + 16·lane.  Issued as inline asm so the
+// compiler's wait-count bookkeeping does not see it: that bookkeeping loses
+// track of which LDS stage a DMA writes at the loop head and would drain every
+// look-ahead load before the next LDS read.  The waits for these loads are
+// placed explicitly (sync_stage).  M0 is set here and not assumed afterwards
+// by compiler-generated code (it is a reserved register there).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const u32x4 *lds) {
+    const uint32_t a = (uint32_t)(uintptr_t)(lds_void *)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(a), "v"(voff), "s"(rs) : "m0");
+}
+#pragma clang diagnostic pop
+
 // ---------------------------------------------------------------------------
-// f16 tile loader: ROWS × 64 halves per step, 16-byte chunks.
+// f16 tile fetched straight into LDS by gfx950's buffer_load_dwordx4 ... lds:
+// ROWS × 64 halves per k-step.  One wave instruction fills 64 consecutive
+// 16-byte LDS slots, lane l the l-th; slot s holds row s/8 at physical chunk
+// s%8, which is logical chunk (s%8) ^ swz(row) of that row.  The 8 lanes of a
+// row therefore fetch its 128 contiguous bytes in a permuted order, and no
+// VGPRs or ds_write instructions are spent on staging.
 // ---------------------------------------------------------------------------
 template <int ROWS>
-struct F16Loader {
-    static constexpr int PER = ROWS * 8 / kThreads;
+struct DmaTile {
+    static constexpr int INSTR = ROWS * 8 / kThreads;   // per wave and k-step
     __amdgpu_buffer_rsrc_t rs;
-    uint32_t off[PER];
-    u32x4 reg[PER];
-    int K;
+    uint32_t off[INSTR];
+    uint32_t kc[INSTR];    // first k of the lane's chunk within a k-step
+    int K, wave;
 
     __device__ void init(const uint16_t *base, int rows_valid, int64_t ld, int K_) {
         K = K_;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         rs = make_rsrc(base, (uint32_t)((rows_valid - 1) * ld * 2 + (int64_t)K_ * 2));
-        const int c = threadIdx.x & 7;
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int r = (i * kThreads + threadIdx.x) >> 3;
+        for (int i = 0; i < INSTR; ++i) {
+            const int s = (i * 4 + wave) * 64 + lane;
+            const int r = s >> 3, c = (s & 7) ^ swz(r);
             off[i] = (uint32_t)(r * ld * 2 + c * 16);
+            kc[i] = c * 8;
         }
     }
-    __device__ __forceinline__ void load(int k0) {
-        const bool ok = k0 + (int)(threadIdx.x & 7) * 8 < K;
+    // live == false: a look-ahead past the last k-step; every lane reads out of
+    // range and the (already consumed) stage is filled with zeros.  Issuing
+    // unconditionally keeps the compiler's per-stage LDS-DMA tracking exact.
+    __device__ __forceinline__ void issue(int k0, u32x4 *stage, bool live = true) const {
+        const uint32_t klim = live ? (uint32_t)K : 0u;   // wave-uniform
 #pragma unroll
-        for (int i = 0; i < PER; ++i) reg[i] = buf_load16(rs, ok ? off[i] + k0 * 2 : kOOB);
-    }
-    __device__ __forceinline__ void store(u32x4 *lds) const {
-        const int c = threadIdx.x & 7;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int r = (i * kThreads + threadIdx.x) >> 3;
-            lds[r * 8 + (c ^ swz(r))] = reg[i];
+        for (int i = 0; i < INSTR; ++i) {
+            const uint32_t o = (uint32_t)k0 + kc[i] < klim ? off[i] + k0 * 2 : kOOB;
+            dma16(rs, o, stage + (i * 4 + wave) * 64);
         }
     }
 };
@@ -342,35 +366,74 @@ struct Q80Loader {
     }
 };
 
-template <int ROWS>
-struct F16BLoader : F16Loader<ROWS> {
-    __device__ void init(const uint8_t *W, int64_t ld, int n0, int rows_valid, int K) {
-        F16Loader<ROWS>::init((const uint16_t *)W + n0 * ld, rows_valid, ld, K);
-    }
-};
-
 template <int ROWS, int FMT>
 struct BLoaderFor;
-template <int ROWS> struct BLoaderFor<ROWS, kFmtF16> { typedef F16BLoader<ROWS> T; };
+template <int ROWS> struct BLoaderFor<ROWS, kFmtF16> { typedef DmaTile<ROWS> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ4_K> { typedef Q4KLoader<ROWS> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ6_K> { typedef Q6KLoader<ROWS> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ8_0> { typedef Q80Loader<ROWS> T; };
 
+// s_waitcnt immediate: at most n vector-memory operations outstanding, every
+// LDS operation done (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+// Stage boundary: wait until this wave has at most N loads in flight and no
+// LDS operation pending, then meet the other waves (N = 0 for LDS-DMA).  The barrier is an asm
+// statement with a memory clobber, so the compiler moves no LDS access across
+// it, but it carries none of __syncthreads' fences, which would also drain
+// the LDS-DMA loads already in flight for the next k-steps.
+template <int N>
+__device__ __forceinline__ void sync_stage() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N));
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// One 64-wide k-step of MFMAs from LDS stage (Ac, Bc) into the wave's tile.
+template <int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x16 (&acc)[FM][FN],
+                                         int wm, int wn, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int c = kk * 2 + (lane >> 5);
+        half8 af[FM], bf[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = wm * TM + i * 32 + (lane & 31);
+            af[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz(r))]);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int r = wn * TN + j * 32 + (lane & 31);
+            bf[j] = __builtin_bit_cast(half8, Bc[r * 8 + (c ^ swz(r))]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+}
+
 // ---------------------------------------------------------------------------
-// The GEMM kernel.
-// ---------------------------------------------------------------------------
+// The GEMM kernel.  Three LDS stages form a ring: while step j is multiplied
+// from stage j%3, the X tile (and the f16 cache tile) of step j+2 streams into
+// stage (j+2)%3 by LDS-DMA.  The fused shape instead loads the raw B bytes of
+// step j+1 into registers during step j and expands them into B stage
+// (j+1)%3 after the step's MFMAs.  One barrier per k-step.
 // PARTIAL: the launch is split along K and writes f32 partial planes (a
 // distinct symbol, so profiles tell the two launch kinds apart).
+// ---------------------------------------------------------------------------
 template <int BM, int BN, int FMT, bool PARTIAL>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
-    constexpr int WN = 2;
-    constexpr int TM = BM / 2, TN = BN / WN;
+    constexpr int TM = BM / 2, TN = BN / 2;
     constexpr int FM = TM / 32, FN = TN / 32;
-    __shared__ u32x4 As[2][BM * 8];
-    __shared__ u32x4 Bs[2][BN * 8];
+    constexpr bool kDmaB = FMT == kFmtF16;
+    __shared__ u32x4 A0[BM * 8], A1[BM * 8], A2[BM * 8];
+    __shared__ u32x4 B0[BN * 8], B1[BN * 8], B2[BN * 8];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave >> 1, wn = wave & 1;
     const int t = xcd_remap(blockIdx.x, gridDim.x);
     const int tiles = a.tiles_m * a.tiles_n;
     const int s = t / tiles, tile = t - s * tiles;
@@ -379,10 +442,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
     const int kt_begin = s * a.steps_per_split;
     const int kt_end = min(kt_begin + a.steps_per_split, a.k_steps);
 
-    F16Loader<BM> la;
+    DmaTile<BM> la;
     la.init(a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
     typename BLoaderFor<BN, FMT>::T lb;
-    lb.init(a.W, a.ldw, n0, min(BN, a.N - n0), a.K);
+    if constexpr (kDmaB)
+        lb.init((const uint16_t *)a.W + n0 * a.ldw, min(BN, a.N - n0), a.ldw, a.K);
+    else
+        lb.init(a.W, a.ldw, n0, min(BN, a.N - n0), a.K);
+    // loads a wave may leave in flight at a stage boundary: the next step's DMA
+    // LDS-DMA loads of one wave are not retired in issue order, so a partial
+    // vmcnt(N) wait does not prove that the older k-step has landed (measured:
+    // wrong, run-to-run different tiles).  Each boundary therefore drains
+    // everything: the DMA of step j+1, issued at the start of step j-1, has one
+    // k-step of MFMA work to arrive in.
+    constexpr int kInflight = 0;
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -390,47 +463,44 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    la.load(kt_begin * kBK);
-    lb.load(kt_begin * kBK);
-    la.store(As[0]);
-    lb.store(Bs[0]);
-    __syncthreads();
-
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int cur = (kt - kt_begin) & 1;
-        const bool more = kt + 1 < kt_end;
-        if (more) {
-            la.load((kt + 1) * kBK);
-            lb.load((kt + 1) * kBK);
-        }
-        const u32x4 *Ac = As[cur];
-        const u32x4 *Bc = Bs[cur];
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int c = kk * 2 + (lane >> 5);
-            half8 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = wm * TM + i * 32 + (lane & 31);
-                af[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz(r))]);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int r = wn * TN + j * 32 + (lane & 31);
-                bf[j] = __builtin_bit_cast(half8, Bc[r * 8 + (c ^ swz(r))]);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (more) {
-            la.store(As[cur ^ 1]);
-            lb.store(Bs[cur ^ 1]);
-        }
-        __syncthreads();
+    // prologue: steps kt_begin and kt_begin + 1 in flight
+    const int k0 = kt_begin * kBK;
+    const bool has_second = kt_begin + 1 < kt_end;
+    if constexpr (!kDmaB) lb.load(k0);
+    la.issue(k0, A0);
+    la.issue(k0 + kBK, A1, has_second);
+    if constexpr (kDmaB) {
+        lb.issue(k0, B0);
+        lb.issue(k0 + kBK, B1, has_second);
+    } else {
+        lb.store(B0);
     }
+
+    auto step = [&](const u32x4 *Ac, const u32x4 *Bc, u32x4 *An, u32x4 *Bn, u32x4 *Bnext,
+                    int kt) {
+        const bool has1 = kt + 1 < kt_end, has2 = kt + 2 < kt_end;
+        sync_stage<kInflight>();
+        if constexpr (!kDmaB) {
+            if (has1) lb.load((kt + 1) * kBK);     // raw B of the next step, before the DMA
+        }
+        la.issue((kt + 2) * kBK, An, has2);
+        if constexpr (kDmaB) lb.issue((kt + 2) * kBK, Bn, has2);
+        mma_step<FM, FN, TM, TN>(Ac, Bc, acc, wm, wn, lane);
+        if constexpr (!kDmaB) {
+            if (has1) lb.store(Bnext);
+        }
+    };
+    for (int kt = kt_begin;;) {
+        step(A0, B0, A2, B2, B1, kt);
+        if (++kt >= kt_end) break;
+        step(A1, B1, A0, B0, B2, kt);
+        if (++kt >= kt_end) break;
+        step(A2, B2, A1, B1, B0, kt);
+        if (++kt >= kt_end) break;
+    }
+    // the look-ahead DMA of the last steps must land before the workgroup's
+    // LDS can be handed to another workgroup
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
     // C layout of a 32x32 MFMA block: lane holds column (lane & 31) and rows
     // 8·(r/4) + 4·(lane/32) + r%4 for accumulator element r.
