@@ -52,7 +52,12 @@ struct Args {
     int tiles_m, tiles_n, k_steps, steps_per_split;
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// LDS chunk swizzle: 16-byte chunk c of row r is stored at position
+// c ^ swz(r).  A ds_read_b128 is served 16 lanes at a time; the 16 lanes of an
+// MFMA operand read 16 consecutive rows at one logical chunk, and this maps
+// them onto 16 distinct 16-byte bank groups (and any 8 consecutive rows onto 8).
+// It depends only on r mod 16, so a lane keeps its chunk across row groups.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
 // range of logical tiles so tiles sharing operands share an L2.
@@ -92,33 +97,32 @@ template <int ROWS>
 struct DmaTile {
     static constexpr int INSTR = ROWS * 8 / kThreads;   // per wave and k-step
     __amdgpu_buffer_rsrc_t rs;
-    uint32_t off[INSTR];
-    uint32_t kc[INSTR];    // first k of the lane's chunk within a k-step
-    int K, wave;
+    uint32_t off0;     // lane's byte offset for instruction 0 at k = 0
+    uint32_t kc;       // first k of the lane's chunk within a k-step
+    uint32_t stride;   // bytes between the row groups of consecutive instructions
+    int K, wave;       // wave index, wave-uniform
 
     __device__ void init(const uint16_t *base, int rows_valid, int64_t ld, int K_) {
         K = K_;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         rs = make_rsrc(base, (uint32_t)((rows_valid - 1) * ld * 2 + (int64_t)K_ * 2));
+        // instruction i fills rows 32i .. 32i+31; this lane fills row 32i + r0
+        // at physical chunk (lane & 7), i.e. logical chunk c (swz(32i + r0) =
+        // swz(r0), so c is the same for every i)
         const int lane = threadIdx.x & 63;
-#pragma unroll
-        for (int i = 0; i < INSTR; ++i) {
-            const int s = (i * 4 + wave) * 64 + lane;
-            const int r = s >> 3, c = (s & 7) ^ swz(r);
-            off[i] = (uint32_t)(r * ld * 2 + c * 16);
-            kc[i] = c * 8;
-        }
+        const int r0 = wave * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r0);
+        off0 = (uint32_t)(r0 * ld * 2 + c * 16);
+        kc = (uint32_t)(c * 8);
+        stride = (uint32_t)(32 * ld * 2);
     }
     // live == false: a look-ahead past the last k-step; every lane reads out of
-    // range and the (already consumed) stage is filled with zeros.  Issuing
-    // unconditionally keeps the compiler's per-stage LDS-DMA tracking exact.
+    // range and the (already consumed) stage is filled with zeros.
     __device__ __forceinline__ void issue(int k0, u32x4 *stage, bool live = true) const {
         const uint32_t klim = live ? (uint32_t)K : 0u;   // wave-uniform
+        const uint32_t o0 = (uint32_t)k0 + kc < klim ? off0 + k0 * 2 : kOOB;
 #pragma unroll
-        for (int i = 0; i < INSTR; ++i) {
-            const uint32_t o = (uint32_t)k0 + kc[i] < klim ? off[i] + k0 * 2 : kOOB;
-            dma16(rs, o, stage + (i * 4 + wave) * 64);
-        }
+        for (int i = 0; i < INSTR; ++i) dma16(rs, o0 + i * stride, stage + (i * 4 + wave) * 64);
     }
 };
 
@@ -153,13 +157,13 @@ struct Q4KLoader {
         rs = make_rsrc(W + (int64_t)n0 * row_bytes, (uint32_t)(rows_valid * row_bytes));
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int r = (i * kThreads + threadIdx.x) >> 1;
+            const int r = (i * kThreads + (int)threadIdx.x) >> 1;
             roff[i] = (uint32_t)(r * row_bytes);
         }
     }
     __device__ __forceinline__ void load(int k0) {
         c4 = (k0 >> 6) & 3;
-        const uint32_t sb = (uint32_t)(k0 >> 8) * 144u, p = threadIdx.x & 1;
+        const uint32_t sb = (uint32_t)(k0 >> 8) * 144u, p = (int)threadIdx.x & 1;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const uint32_t o = roff[i] + sb;
@@ -168,10 +172,10 @@ struct Q4KLoader {
         }
     }
     __device__ __forceinline__ void store(u32x4 *lds) const {
-        const int p = threadIdx.x & 1;
+        const int p = (int)threadIdx.x & 1;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int r = (i * kThreads + threadIdx.x) >> 1;
+            const int r = (i * kThreads + (int)threadIdx.x) >> 1;
             const u32x4 h = hdr[i];
             uint32_t sc0, m0, sc1, m1;
             if (c4 < 2) {  // sub-blocks 2c4, 2c4+1 < 4: low 6 bits of s[j] / s[j+4]
@@ -249,13 +253,13 @@ struct Q6KLoader {
         rs = make_rsrc(W + start - shift0, (uint32_t)((extent + 3) & ~(int64_t)3));
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int r = (i * kThreads + threadIdx.x) >> 1;
+            const int r = (i * kThreads + (int)threadIdx.x) >> 1;
             roff[i] = shift0 + (uint32_t)(r * row_bytes);
         }
     }
     __device__ __forceinline__ void load(int k0) {
         c4 = (k0 >> 6) & 3;
-        const uint32_t h = c4 >> 1, gp = c4 & 1, p = threadIdx.x & 1;
+        const uint32_t h = c4 >> 1, gp = c4 & 1, p = (int)threadIdx.x & 1;
         const uint32_t sb = (uint32_t)(k0 >> 8) * 210u;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -272,13 +276,13 @@ struct Q6KLoader {
         }
     }
     __device__ __forceinline__ void store(u32x4 *lds) const {
-        const int p = threadIdx.x & 1;
+        const int p = (int)threadIdx.x & 1;
         const uint32_t gp = c4 & 1;
         const uint32_t n4 = gp ? 4 : 0, sh_a = 4 * gp, sh_b = 4 * gp + 2;
         const uint32_t L = 0x0F0F0F0Fu, H = 0x03030303u;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int r = (i * kThreads + threadIdx.x) >> 1;
+            const int r = (i * kThreads + (int)threadIdx.x) >> 1;
             const bool oh = odd[i] != 0;
             const u32x4 a = realign16(wa[i], oh), b = realign16(wb[i], oh), hh = realign16(wh[i], oh);
             const uint32_t bsa = 8 * osc[i], bsb = 8 * ((osc[i] + 2) & 3);
@@ -331,12 +335,12 @@ struct Q80Loader {
         rs = make_rsrc(W + start - shift0, (uint32_t)((extent + 3) & ~(int64_t)3));
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int r = (i * kThreads + threadIdx.x) >> 1;
+            const int r = (i * kThreads + (int)threadIdx.x) >> 1;
             roff[i] = shift0 + (uint32_t)(r * row_bytes);
         }
     }
     __device__ __forceinline__ void load(int k0) {
-        const int b = (k0 >> 5) + (int)(threadIdx.x & 1);
+        const int b = (k0 >> 5) + ((int)threadIdx.x & 1);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const uint32_t o = roff[i] + (uint32_t)b * 34u;
@@ -349,10 +353,10 @@ struct Q80Loader {
         }
     }
     __device__ __forceinline__ void store(u32x4 *lds) const {
-        const int p = threadIdx.x & 1;
+        const int p = (int)threadIdx.x & 1;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int r = (i * kThreads + threadIdx.x) >> 1;
+            const int r = (i * kThreads + (int)threadIdx.x) >> 1;
             const bool oh = odd[i] != 0;
             const float d = f16_bits_to_f32(oh ? (w[i][0] >> 16) : w[i][0]);
             uint32_t q[8];
@@ -389,29 +393,45 @@ __device__ __forceinline__ void sync_stage() {
     asm volatile("s_barrier" ::: "memory");
 }
 
+// MFMA operand fragments of one 16-wide k-slice.
+template <int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void load_frags(const u32x4 *Ac, const u32x4 *Bc, int kk, int wm,
+                                           int wn, int lane, half8 (&af)[FM], half8 (&bf)[FN]) {
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int r = wm * TM + i * 32 + (lane & 31);
+        af[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz(r))]);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int r = wn * TN + j * 32 + (lane & 31);
+        bf[j] = __builtin_bit_cast(half8, Bc[r * 8 + (c ^ swz(r))]);
+    }
+}
+
 // One 64-wide k-step of MFMAs from LDS stage (Ac, Bc) into the wave's tile.
+// Fragments are double-buffered: the LDS reads of k-slice kk+1 are issued
+// before the MFMAs of slice kk (scheduling barriers keep that order), so their
+// latency hides behind matrix work.
 template <int FM, int FN, int TM, int TN>
 __device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x16 (&acc)[FM][FN],
                                          int wm, int wn, int lane) {
+    half8 af[2][FM], bf[2][FN];
+    load_frags<FM, FN, TM, TN>(Ac, Bc, 0, wm, wn, lane, af[0], bf[0]);
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int c = kk * 2 + (lane >> 5);
-        half8 af[FM], bf[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int r = wm * TM + i * 32 + (lane & 31);
-            af[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz(r))]);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int r = wn * TN + j * 32 + (lane & 31);
-            bf[j] = __builtin_bit_cast(half8, Bc[r * 8 + (c ^ swz(r))]);
-        }
+        const int cur = kk & 1;
+        if (kk + 1 < kBK / 16)
+            load_frags<FM, FN, TM, TN>(Ac, Bc, kk + 1, wm, wn, lane, af[cur ^ 1], bf[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], bf[cur][j], acc[i][j],
+                                                                   0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -449,14 +469,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
         lb.init((const uint16_t *)a.W + n0 * a.ldw, min(BN, a.N - n0), a.ldw, a.K);
     else
         lb.init(a.W, a.ldw, n0, min(BN, a.N - n0), a.K);
-    // loads a wave may leave in flight at a stage boundary: the next step's DMA
-    // LDS-DMA loads of one wave are not retired in issue order, so a partial
-    // vmcnt(N) wait does not prove that the older k-step has landed (measured:
-    // wrong, run-to-run different tiles).  Each boundary therefore drains
-    // everything: the DMA of step j+1, issued at the start of step j-1, has one
-    // k-step of MFMA work to arrive in.
-    constexpr int kInflight = 0;
-
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -476,10 +488,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
         lb.store(B0);
     }
 
+    // Step kt on stage (kt - kt_begin) % 3.  LDS-DMA loads of one wave retire
+    // out of issue order (a partial vmcnt wait gave wrong, run-to-run
+    // different tiles), so each boundary drains this wave's loads to zero:
+    // the DMA of step kt+1, issued at the start of step kt-1, has one k-step
+    // of MFMA work to land in.  The fused shape loads the raw B bytes of step
+    // kt+1 in registers during step kt and expands them into B stage
+    // (kt+1) % 3 after the step's MFMAs.
     auto step = [&](const u32x4 *Ac, const u32x4 *Bc, u32x4 *An, u32x4 *Bn, u32x4 *Bnext,
                     int kt) {
         const bool has1 = kt + 1 < kt_end, has2 = kt + 2 < kt_end;
-        sync_stage<kInflight>();
+        sync_stage<0>();
         if constexpr (!kDmaB) {
             if (has1) lb.load((kt + 1) * kBK);     // raw B of the next step, before the DMA
         }
@@ -498,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
         step(A2, B2, A1, B1, B0, kt);
         if (++kt >= kt_end) break;
     }
-    // the look-ahead DMA of the last steps must land before the workgroup's
+    // the look-ahead loads of the last steps must land before the workgroup's
     // LDS can be handed to another workgroup
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
