@@ -509,14 +509,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
             if (has1) lb.store(Bnext);
         }
     };
-    for (int kt = kt_begin;;) {
+    // A single-exit loop over whole rounds of the three stages, then the tail:
+    // with the exits inside the round, the compiler keeps the accumulators in
+    // VGPRs across the back edge and copies all of them to and from AGPRs on
+    // every round.
+    int kt = kt_begin;
+    for (const int rounds_end = kt_begin + (kt_end - kt_begin) / 3 * 3; kt < rounds_end; kt += 3) {
         step(A0, B0, A2, B2, B1, kt);
-        if (++kt >= kt_end) break;
-        step(A1, B1, A0, B0, B2, kt);
-        if (++kt >= kt_end) break;
-        step(A2, B2, A1, B1, B0, kt);
-        if (++kt >= kt_end) break;
+        step(A1, B1, A0, B0, B2, kt + 1);
+        step(A2, B2, A1, B1, B0, kt + 2);
     }
+    if (kt < kt_end) step(A0, B0, A2, B2, B1, kt);
+    if (kt + 1 < kt_end) step(A1, B1, A0, B0, B2, kt + 1);
     // the look-ahead loads of the last steps must land before the workgroup's
     // LDS can be handed to another workgroup
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
