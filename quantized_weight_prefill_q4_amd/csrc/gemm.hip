@@ -33,11 +33,13 @@
 #include "mq_device.h"
 #include "mq_internal.h"
 
+#include <type_traits>
+
 namespace mq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;        // k elements per step
+constexpr int kBK = 64;        // k elements per step of the fused (quantized-B) kernels
 constexpr int kCUs = 256;      // MI355X compute units
 constexpr int kXCDs = 8;
 
@@ -52,12 +54,20 @@ struct Args {
     int tiles_m, tiles_n, k_steps, steps_per_split;
 };
 
-// LDS chunk swizzle: 16-byte chunk c of row r is stored at position
-// c ^ swz(r).  A ds_read_b128 is served 16 lanes at a time; the 16 lanes of an
-// MFMA operand read 16 consecutive rows at one logical chunk, and this maps
-// them onto 16 distinct 16-byte bank groups (and any 8 consecutive rows onto 8).
-// It depends only on r mod 16, so a lane keeps its chunk across row groups.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// LDS tiles are rows of CPR 16-byte chunks (CPR = k-step / 8: 8 for a 64-wide
+// step, 4 for a 32-wide one); chunk c of row r is stored at position
+// c ^ swz<CPR>(r).  The LDS (64 banks of 4 bytes) serves a ds_read_b128 16
+// lanes at a time, and the 16 lanes of an MFMA operand read 16 consecutive
+// rows at one logical chunk: the swizzle puts them on 16 distinct 16-byte
+// bank groups.  It depends only on r mod 16, so a lane that loads rows r0,
+// r0 + 32, ... (or r0 + 64, ...) keeps the same chunk.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (CPR == 8)
+        return (r & 7) ^ ((r >> 3) & 1);   // row = 128 B: bank group 8·(r&1) + position
+    else
+        return (r >> 2) & 3;               // row = 64 B: bank group 4·(r&3) + position
+}
 
 // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
 // range of logical tiles so tiles sharing operands share an L2.
@@ -85,17 +95,31 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, 
 }
 #pragma clang diagnostic pop
 
+// Logical tile -> (M tile, N tile).  Tiles are taken in groups of kGroupM
+// M-tiles, N-tile by N-tile: the 32 tiles an XCD runs at once then cover
+// 4 M-tiles × 8 N-tiles, whose operands (4 X panels + 8 W panels per k-step)
+// are shared through that XCD's L2 with fewer misses than 8 × 4 would have.
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int per_group = kGroupM * tiles_n;
+    const int g = tile / per_group, r = tile - g * per_group;
+    const int gm = min(kGroupM, tiles_m - g * kGroupM);   // the last group may be narrower
+    tn = r / gm;
+    tm = g * kGroupM + (r - tn * gm);
+}
+
 // ---------------------------------------------------------------------------
 // f16 tile fetched straight into LDS by gfx950's buffer_load_dwordx4 ... lds:
-// ROWS × 64 halves per k-step.  One wave instruction fills 64 consecutive
-// 16-byte LDS slots, lane l the l-th; slot s holds row s/8 at physical chunk
-// s%8, which is logical chunk (s%8) ^ swz(row) of that row.  The 8 lanes of a
-// row therefore fetch its 128 contiguous bytes in a permuted order, and no
+// ROWS × 8·CPR halves per k-step.  One wave instruction fills 64 consecutive
+// 16-byte LDS slots, lane l the l-th; slot s holds row s/CPR at physical chunk
+// s%CPR, which is logical chunk (s%CPR) ^ swz(row) of that row.  The lanes of
+// a row therefore fetch its contiguous bytes in a permuted order, and no
 // VGPRs or ds_write instructions are spent on staging.
 // ---------------------------------------------------------------------------
-template <int ROWS>
+template <int ROWS, int CPR>
 struct DmaTile {
-    static constexpr int INSTR = ROWS * 8 / kThreads;   // per wave and k-step
+    static constexpr int RPI = 64 / CPR;                  // rows per wave instruction
+    static constexpr int INSTR = ROWS * CPR / kThreads;   // per wave and k-step
     __amdgpu_buffer_rsrc_t rs;
     uint32_t off0;     // lane's byte offset for instruction 0 at k = 0
     uint32_t kc;       // first k of the lane's chunk within a k-step
@@ -106,21 +130,22 @@ struct DmaTile {
         K = K_;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         rs = make_rsrc(base, (uint32_t)((rows_valid - 1) * ld * 2 + (int64_t)K_ * 2));
-        // instruction i fills rows 32i .. 32i+31; this lane fills row 32i + r0
-        // at physical chunk (lane & 7), i.e. logical chunk c (swz(32i + r0) =
-        // swz(r0), so c is the same for every i)
+        // instruction i fills rows 4·RPI·i + RPI·wave + (0 .. RPI-1); this lane
+        // fills row r0 + 4·RPI·i at physical chunk lane % CPR, i.e. logical
+        // chunk c (the swizzle of r0 + 4·RPI·i equals that of r0)
         const int lane = threadIdx.x & 63;
-        const int r0 = wave * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r0);
+        const int r0 = wave * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swz<CPR>(r0);
         off0 = (uint32_t)(r0 * ld * 2 + c * 16);
         kc = (uint32_t)(c * 8);
-        stride = (uint32_t)(32 * ld * 2);
+        stride = (uint32_t)(4 * RPI * ld * 2);
     }
     // live == false: a look-ahead past the last k-step; every lane reads out of
     // range and the (already consumed) stage is filled with zeros.
     __device__ __forceinline__ void issue(int k0, u32x4 *stage, bool live = true) const {
         const uint32_t klim = live ? (uint32_t)K : 0u;   // wave-uniform
         const uint32_t o0 = (uint32_t)k0 + kc < klim ? off0 + k0 * 2 : kOOB;
+        static_assert(INSTR * 4 * 64 == ROWS * CPR, "tile rows must fill whole instructions");
 #pragma unroll
         for (int i = 0; i < INSTR; ++i) dma16(rs, o0 + i * stride, stage + (i * 4 + wave) * 64);
     }
@@ -197,7 +222,7 @@ struct Q4KLoader {
             const u32x4 q = qs[i];
             const uint32_t L = 0x0F0F0F0Fu;
             u32x4 *row = lds + r * 8;
-            const int sw = swz(r);
+            const int sw = swz<8>(r);
             row[(2 * p) ^ sw] = q4k_chunk(q.x & L, q.y & L, A0, C0);
             row[(2 * p + 1) ^ sw] = q4k_chunk(q.z & L, q.w & L, A0, C0);
             row[(4 + 2 * p) ^ sw] = q4k_chunk((q.x >> 4) & L, (q.y >> 4) & L, A1, C1);
@@ -299,7 +324,7 @@ struct Q6KLoader {
             const uint32_t qb2 = ((b.z >> n4) & L) | (((hh.z >> sh_b) & H) << 4);
             const uint32_t qb3 = ((b.w >> n4) & L) | (((hh.w >> sh_b) & H) << 4);
             u32x4 *row = lds + r * 8;
-            const int sw = swz(r);
+            const int sw = swz<8>(r);
             row[(2 * p) ^ sw] = q6k_chunk(qa0, qa1, dsa);
             row[(2 * p + 1) ^ sw] = q6k_chunk(qa2, qa3, dsa);
             row[(4 + 2 * p) ^ sw] = q6k_chunk(qb0, qb1, dsb);
@@ -363,7 +388,7 @@ struct Q80Loader {
 #pragma unroll
             for (int j = 0; j < 8; ++j) q[j] = oh ? w[i][j + 1] : shift2(w[i][j + 1], w[i][j]);
             u32x4 *row = lds + r * 8;
-            const int sw = swz(r);
+            const int sw = swz<8>(r);
 #pragma unroll
             for (int j = 0; j < 4; ++j) row[(4 * p + j) ^ sw] = q80_chunk(q[2 * j], q[2 * j + 1], d);
         }
@@ -372,7 +397,7 @@ struct Q80Loader {
 
 template <int ROWS, int FMT>
 struct BLoaderFor;
-template <int ROWS> struct BLoaderFor<ROWS, kFmtF16> { typedef DmaTile<ROWS> T; };
+template <int ROWS> struct BLoaderFor<ROWS, kFmtF16> { typedef DmaTile<ROWS, 8> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ4_K> { typedef Q4KLoader<ROWS> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ6_K> { typedef Q6KLoader<ROWS> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ8_0> { typedef Q80Loader<ROWS> T; };
@@ -394,36 +419,36 @@ __device__ __forceinline__ void sync_stage() {
 }
 
 // MFMA operand fragments of one 16-wide k-slice.
-template <int FM, int FN, int TM, int TN>
+template <int FM, int FN, int TM, int TN, int CPR>
 __device__ __forceinline__ void load_frags(const u32x4 *Ac, const u32x4 *Bc, int kk, int wm,
                                            int wn, int lane, half8 (&af)[FM], half8 (&bf)[FN]) {
     const int c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int r = wm * TM + i * 32 + (lane & 31);
-        af[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz(r))]);
+        af[i] = __builtin_bit_cast(half8, Ac[r * CPR + (c ^ swz<CPR>(r))]);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int r = wn * TN + j * 32 + (lane & 31);
-        bf[j] = __builtin_bit_cast(half8, Bc[r * 8 + (c ^ swz(r))]);
+        bf[j] = __builtin_bit_cast(half8, Bc[r * CPR + (c ^ swz<CPR>(r))]);
     }
 }
 
-// One 64-wide k-step of MFMAs from LDS stage (Ac, Bc) into the wave's tile.
+// One k-step (8·CPR wide) of MFMAs from LDS stage (Ac, Bc) into the wave's tile.
 // Fragments are double-buffered: the LDS reads of k-slice kk+1 are issued
 // before the MFMAs of slice kk (scheduling barriers keep that order), so their
 // latency hides behind matrix work.
-template <int FM, int FN, int TM, int TN>
+template <int FM, int FN, int TM, int TN, int CPR>
 __device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x16 (&acc)[FM][FN],
                                          int wm, int wn, int lane) {
     half8 af[2][FM], bf[2][FN];
-    load_frags<FM, FN, TM, TN>(Ac, Bc, 0, wm, wn, lane, af[0], bf[0]);
+    load_frags<FM, FN, TM, TN, CPR>(Ac, Bc, 0, wm, wn, lane, af[0], bf[0]);
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+    for (int kk = 0; kk < CPR / 2; ++kk) {
         const int cur = kk & 1;
-        if (kk + 1 < kBK / 16)
-            load_frags<FM, FN, TM, TN>(Ac, Bc, kk + 1, wm, wn, lane, af[cur ^ 1], bf[cur ^ 1]);
+        if (kk + 1 < CPR / 2)
+            load_frags<FM, FN, TM, TN, CPR>(Ac, Bc, kk + 1, wm, wn, lane, af[cur ^ 1], bf[cur ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -444,27 +469,32 @@ __device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x1
 // PARTIAL: the launch is split along K and writes f32 partial planes (a
 // distinct symbol, so profiles tell the two launch kinds apart).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int FMT, bool PARTIAL>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
+// BK: k-step width (64, or 32 for the f16 operands when two workgroups share
+// a compute unit: 72 KB of LDS and at most 256 registers per wave each).
+template <int BM, int BN, int FMT, bool PARTIAL, int BK>
+__global__ __launch_bounds__(kThreads, BK == 32 ? 2 : 1) void gemm_kernel(Args a) {
     constexpr int TM = BM / 2, TN = BN / 2;
     constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int CPR = BK / 8;
     constexpr bool kDmaB = FMT == kFmtF16;
-    __shared__ u32x4 A0[BM * 8], A1[BM * 8], A2[BM * 8];
-    __shared__ u32x4 B0[BN * 8], B1[BN * 8], B2[BN * 8];
+    static_assert(kDmaB || BK == 64, "the fused loaders expand 64-wide k-steps");
+    __shared__ u32x4 A0[BM * CPR], A1[BM * CPR], A2[BM * CPR];
+    __shared__ u32x4 B0[BN * CPR], B1[BN * CPR], B2[BN * CPR];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int t = xcd_remap(blockIdx.x, gridDim.x);
     const int tiles = a.tiles_m * a.tiles_n;
     const int s = t / tiles, tile = t - s * tiles;
-    const int tn = tile / a.tiles_m, tm = tile - tn * a.tiles_m;
+    int tm, tn;
+    tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt_begin = s * a.steps_per_split;
     const int kt_end = min(kt_begin + a.steps_per_split, a.k_steps);
 
-    DmaTile<BM> la;
+    DmaTile<BM, CPR> la;
     la.init(a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
-    typename BLoaderFor<BN, FMT>::T lb;
+    typename std::conditional<kDmaB, DmaTile<BN, CPR>, typename BLoaderFor<BN, FMT>::T>::type lb;
     if constexpr (kDmaB)
         lb.init((const uint16_t *)a.W + n0 * a.ldw, min(BN, a.N - n0), a.ldw, a.K);
     else
@@ -476,14 +506,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
     // prologue: steps kt_begin and kt_begin + 1 in flight
-    const int k0 = kt_begin * kBK;
+    const int k0 = kt_begin * BK;
     const bool has_second = kt_begin + 1 < kt_end;
     if constexpr (!kDmaB) lb.load(k0);
     la.issue(k0, A0);
-    la.issue(k0 + kBK, A1, has_second);
+    la.issue(k0 + BK, A1, has_second);
     if constexpr (kDmaB) {
         lb.issue(k0, B0);
-        lb.issue(k0 + kBK, B1, has_second);
+        lb.issue(k0 + BK, B1, has_second);
     } else {
         lb.store(B0);
     }
@@ -500,11 +530,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Args a) {
         const bool has1 = kt + 1 < kt_end, has2 = kt + 2 < kt_end;
         sync_stage<0>();
         if constexpr (!kDmaB) {
-            if (has1) lb.load((kt + 1) * kBK);     // raw B of the next step, before the DMA
+            if (has1) lb.load((kt + 1) * BK);     // raw B of the next step, before the DMA
         }
-        la.issue((kt + 2) * kBK, An, has2);
-        if constexpr (kDmaB) lb.issue((kt + 2) * kBK, Bn, has2);
-        mma_step<FM, FN, TM, TN>(Ac, Bc, acc, wm, wn, lane);
+        la.issue((kt + 2) * BK, An, has2);
+        if constexpr (kDmaB) lb.issue((kt + 2) * BK, Bn, has2);
+        mma_step<FM, FN, TM, TN, CPR>(Ac, Bc, acc, wm, wn, lane);
         if constexpr (!kDmaB) {
             if (has1) lb.store(Bnext);
         }
@@ -555,12 +585,19 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ w
     Y[(int64_t)m * ldy + n] = acc;
 }
 
+// k-step width per operand kind: 32 for the f16 cache (two workgroups per
+// compute unit), 64 for the fused kernels
+constexpr int bk_for(int fmt) { return fmt == kFmtF16 ? 64 : 64; }
+
 template <int BM, int FMT>
 hipError_t launch_tile(const Args &a, int grid, bool partial, hipStream_t stream) {
+    constexpr int BK = bk_for(FMT);
     if (partial)
-        hipLaunchKernelGGL((gemm_kernel<BM, 128, FMT, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, 128, FMT, true, BK>), dim3(grid), dim3(kThreads), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, 128, FMT, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, 128, FMT, false, BK>), dim3(grid), dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
@@ -576,13 +613,15 @@ hipError_t launch_fmt(const Args &a, int bm, int grid, bool partial, hipStream_t
 }  // namespace
 
 GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req) {
-    (void)fmt;
     GemmPlan p;
     p.bn = 128;
     p.bm = M > 128 ? 256 : (M > 64 ? 128 : 64);
     p.tiles_m = (M + p.bm - 1) / p.bm;
     p.tiles_n = (N + p.bn - 1) / p.bn;
-    p.k_steps = (K + kBK - 1) / kBK;
+    // The K split is planned in 64-element units whatever the kernel's k-step,
+    // so the f16-cache and fused kernels partition K identically and sum the
+    // same products in the same order.
+    const int k64 = (K + 63) / 64;
     int split = split_req;
     if (split == 0) {
         split = 1;
@@ -590,14 +629,17 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req) {
         if (tiles < kCUs && (int64_t)M * N <= (1 << 26)) {
             split = (int)(kCUs / tiles);
             if (split > 16) split = 16;
-            const int max_by_k = p.k_steps / 4;   // keep >= 4 k-steps per partition
+            const int max_by_k = k64 / 4;   // keep >= 256 k per partition
             if (split > max_by_k) split = max_by_k;
             if (split < 1) split = 1;
         }
     }
-    if (split > p.k_steps) split = p.k_steps;
-    p.steps_per_split = (p.k_steps + split - 1) / split;
-    p.split = (p.k_steps + p.steps_per_split - 1) / p.steps_per_split;
+    if (split > k64) split = k64;
+    const int per64 = (k64 + split - 1) / split;
+    p.split = (k64 + per64 - 1) / per64;
+    const int bk = bk_for(fmt);
+    p.k_steps = (K + bk - 1) / bk;
+    p.steps_per_split = per64 * (64 / bk);
     p.ws_bytes = p.split > 1 ? (int64_t)p.split * M * N * 4 : 0;
     return p;
 }
