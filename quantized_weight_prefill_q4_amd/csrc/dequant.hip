@@ -6,15 +6,14 @@
 // llama.cpp PR #57, Summary: the cache row may be padded by one 128-byte line.
 //
 // The pass is HBM-bound (0.56–1.06 B read and 2 B written per element), so
-// the kernel is laid out for the memory system, not for arithmetic:
-//   * one thread produces one 16-byte run of 8 consecutive f16 outputs, so a
-//     wave writes 1 KiB of contiguous cache row per store instruction;
-//   * Q4_K blocks (144 B) are 16-byte aligned and are read with 16/8-byte
-//     loads; Q6_K (210 B) and Q8_0 (34 B) blocks are only 2-byte aligned, so
-//     their bytes are read as the aligned dwords that contain them and
-//     re-assembled with v_alignbyte (a dword that holds a requested byte lies
-//     on the same page as that byte, so no load can fault).
-//   * the pad columns [K, ld) are written as +0 by the tail of the same grid.
+// the kernel is laid out for the memory system, not for arithmetic: each
+// workgroup stages the contiguous bytes of its blocks in LDS with one 16-byte
+// load per 16 input bytes, then every thread decodes four 16-byte runs of
+// f16 output, each wave store writing 1 KiB of contiguous cache row.  Q6_K
+// (210 B) and Q8_0 (34 B) blocks are only 2-byte aligned; they are read from
+// LDS with 2-byte accesses, and global memory is only read in aligned
+// 16-byte chunks.  The pad columns [K, ld) are written as +0 by the tail of
+// the grid.
 
 #include "mq_device.h"
 #include "mq_internal.h"
@@ -23,17 +22,22 @@ namespace mq {
 namespace {
 
 constexpr uint32_t kThreads = 256;
+constexpr uint32_t kChunksPerThread = 4;                        // 16-byte output runs
+constexpr uint32_t kChunksPerGroup = kThreads * kChunksPerThread;   // 16 KiB of f16 out
 
-// 8 bytes at a 2-byte-aligned address as two little-endian dwords.
-__device__ __forceinline__ u32x2 load8_a2(const uint8_t *p) {
-    const uintptr_t a = (uintptr_t)p;
-    const uint32_t *w = (const uint32_t *)(a & ~(uintptr_t)3);
-    const uint32_t w0 = w[0], w1 = w[1];
-    if (a & 2) {
-        const uint32_t w2 = w[2];
-        return u32x2{shift2(w1, w0), shift2(w2, w1)};
-    }
-    return u32x2{w0, w1};
+template <int FMT> struct Fmt;
+template <> struct Fmt<kFmtQ4_K> { static constexpr uint32_t BE = 256, BB = 144; };
+template <> struct Fmt<kFmtQ6_K> { static constexpr uint32_t BE = 256, BB = 210; };
+template <> struct Fmt<kFmtQ8_0> { static constexpr uint32_t BE = 32, BB = 34; };
+
+// blocks per workgroup and their staged bytes (plus up to 16 bytes of lead-in)
+template <int FMT> constexpr uint32_t group_blocks() { return kChunksPerGroup * 8 / Fmt<FMT>::BE; }
+template <int FMT> constexpr uint32_t stage_bytes() { return group_blocks<FMT>() * Fmt<FMT>::BB + 32; }
+
+// little-endian reads from LDS at a 2-byte-aligned address
+__device__ __forceinline__ uint32_t lds_u16(const uint8_t *p) { return *(const uint16_t *)p; }
+__device__ __forceinline__ uint32_t lds_u32_a2(const uint8_t *p) {
+    return lds_u16(p) | (lds_u16(p + 2) << 16);
 }
 
 __device__ __forceinline__ void store8(uint16_t *o, const float v[8]) {
@@ -41,34 +45,15 @@ __device__ __forceinline__ void store8(uint16_t *o, const float v[8]) {
                         pack_f16x2(v[6], v[7])};
 }
 
-// Zero one 8-element run of the pad columns [K, ld).
-__device__ __forceinline__ void write_pad(uint16_t *out, uint32_t p, uint32_t per_row, uint32_t K,
-                                          uint32_t ld) {
-    const uint32_t row = p / per_row, c = p - row * per_row;
-    *(u32x4 *)(out + (size_t)row * ld + K + 8 * c) = u32x4{0, 0, 0, 0};
-}
-
-// Q4_K: 256 elements = 8 sub-blocks of 32; value fl32(d·sc·q − dmin·m).
-// Element e takes the low nibble of qs[32·(e/64) + e%32] when e%64 < 32, the
-// high nibble otherwise; (sc, m) of sub-block j come from the 12 scale bytes
-// (6 bits each; sub-blocks 4..7 split 4 + 2 bits).
-__global__ __launch_bounds__(kThreads) void dequant_q4k(const uint8_t *__restrict__ wq,
-                                                        uint16_t *__restrict__ out, uint32_t nb,
-                                                        uint32_t K, uint32_t ld, uint32_t n_data,
-                                                        uint32_t pad_per_row, uint32_t n_total) {
-    const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
-    if (u >= n_total) return;
-    if (u >= n_data) {
-        write_pad(out, u - n_data, pad_per_row, K, ld);
-        return;
-    }
-    const uint32_t g = u >> 5, e0 = (u & 31) * 8;
-    const uint32_t row = g / nb, kb = g - row * nb;
-    const uint8_t *blk = wq + (size_t)g * 144;
+// Q4_K, 8 outputs e0..e0+7 of the block at `blk` (16-byte aligned in LDS):
+// value fl32(d·sc·q − dmin·m).  Element e takes the low nibble of
+// qs[32·(e/64) + e%32] when e%64 < 32, the high nibble otherwise; (sc, m) of
+// sub-block j come from the 12 scale bytes (6 bits each; sub-blocks 4..7
+// split 4 + 2 bits).
+__device__ __forceinline__ void decode_q4k(const uint8_t *blk, uint32_t e0, float v[8]) {
     const u32x4 h = *(const u32x4 *)blk;
     const uint32_t c = e0 >> 6, r = e0 & 63, j = e0 >> 5;
     const u32x2 qq = *(const u32x2 *)(blk + 16 + 32 * c + (r & 31));
-
     const uint32_t sh = 8 * (j & 3);
     const uint32_t s_lo = (h.y >> sh) & 0xFF;   // s[j & 3]
     const uint32_t s_mid = (h.z >> sh) & 0xFF;  // s[(j & 3) + 4]
@@ -77,11 +62,9 @@ __global__ __launch_bounds__(kThreads) void dequant_q4k(const uint8_t *__restric
     const uint32_t m = j < 4 ? (s_mid & 63) : ((s_hi >> 4) | ((s_mid >> 6) << 4));
     const float A = f16_bits_to_f32(h.x) * (float)sc;          // exact
     const float C = f16_bits_to_f32(h.x >> 16) * (float)m;     // exact
-
     const uint32_t n4 = (r >= 32) ? 4 : 0;
     const uint32_t w0 = (qq.x >> n4) & 0x0F0F0F0Fu, w1 = (qq.y >> n4) & 0x0F0F0F0Fu;
-    float v[8];
-    // A·q is exact, so one fused rounding equals fl32(A·q − C).
+    // A·q is exact, so one fused rounding equals fl32(A·q − C)
     v[0] = __builtin_fmaf(A, ubyte_f32<0>(w0), -C);
     v[1] = __builtin_fmaf(A, ubyte_f32<1>(w0), -C);
     v[2] = __builtin_fmaf(A, ubyte_f32<2>(w0), -C);
@@ -90,37 +73,25 @@ __global__ __launch_bounds__(kThreads) void dequant_q4k(const uint8_t *__restric
     v[5] = __builtin_fmaf(A, ubyte_f32<1>(w1), -C);
     v[6] = __builtin_fmaf(A, ubyte_f32<2>(w1), -C);
     v[7] = __builtin_fmaf(A, ubyte_f32<3>(w1), -C);
-    store8(out + (size_t)row * ld + kb * 256 + e0, v);
 }
 
-// Q6_K: element e = 128h + 32g + l takes its low 4 bits from
-// ql[64h + l + 32(g & 1)] (low nibble for g < 2, high for g >= 2), its high 2
-// bits from qh[32h + l] >> 2g, and the int8 scale sc[e / 16]; the value is
-// (d·sc)·(q − 32) in f32 (exact; IEEE signed zeros kept).
-__global__ __launch_bounds__(kThreads) void dequant_q6k(const uint8_t *__restrict__ wq,
-                                                        uint16_t *__restrict__ out, uint32_t nb,
-                                                        uint32_t K, uint32_t ld, uint32_t n_data,
-                                                        uint32_t pad_per_row, uint32_t n_total) {
-    const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
-    if (u >= n_total) return;
-    if (u >= n_data) {
-        write_pad(out, u - n_data, pad_per_row, K, ld);
-        return;
-    }
-    const uint32_t g = u >> 5, e0 = (u & 31) * 8;
-    const uint32_t row = g / nb, kb = g - row * nb;
-    const uint8_t *blk = wq + (size_t)g * 210;
+// Q6_K, 8 outputs of the block at `blk` (2-byte aligned in LDS): element
+// e = 128h + 32g + l takes its low 4 bits from ql[64h + l + 32(g & 1)] (low
+// nibble for g < 2, high for g >= 2), its high 2 bits from qh[32h + l] >> 2g,
+// and the int8 scale sc[e / 16]; value (d·sc)·(q − 32) in f32 (exact; IEEE
+// signed zeros kept).
+__device__ __forceinline__ void decode_q6k(const uint8_t *blk, uint32_t e0, float v[8]) {
     const uint32_t h = e0 >> 7, grp = (e0 >> 5) & 3, l0 = e0 & 31;
-    const u32x2 lo = load8_a2(blk + 64 * h + l0 + 32 * (grp & 1));
-    const u32x2 hi = load8_a2(blk + 128 + 32 * h + l0);
+    const uint8_t *lo = blk + 64 * h + l0 + 32 * (grp & 1);
+    const uint8_t *hi = blk + 128 + 32 * h + l0;
+    const uint32_t lo0 = lds_u32_a2(lo), lo1 = lds_u32_a2(lo + 4);
+    const uint32_t hi0 = lds_u32_a2(hi), hi1 = lds_u32_a2(hi + 4);
     const float s = (float)(int)(int8_t)blk[192 + (e0 >> 4)];
-    const float d = f16_bits_to_f32(*(const uint16_t *)(blk + 208));
+    const float d = f16_bits_to_f32(lds_u16(blk + 208));
     const float ds = d * s;  // exact
-
     const uint32_t n4 = grp >= 2 ? 4 : 0, h2 = 2 * grp;
-    const uint32_t q0 = ((lo.x >> n4) & 0x0F0F0F0Fu) | (((hi.x >> h2) & 0x03030303u) << 4);
-    const uint32_t q1 = ((lo.y >> n4) & 0x0F0F0F0Fu) | (((hi.y >> h2) & 0x03030303u) << 4);
-    float v[8];
+    const uint32_t q0 = ((lo0 >> n4) & 0x0F0F0F0Fu) | (((hi0 >> h2) & 0x03030303u) << 4);
+    const uint32_t q1 = ((lo1 >> n4) & 0x0F0F0F0Fu) | (((hi1 >> h2) & 0x03030303u) << 4);
     v[0] = ds * (ubyte_f32<0>(q0) - 32.0f);
     v[1] = ds * (ubyte_f32<1>(q0) - 32.0f);
     v[2] = ds * (ubyte_f32<2>(q0) - 32.0f);
@@ -129,63 +100,116 @@ __global__ __launch_bounds__(kThreads) void dequant_q6k(const uint8_t *__restric
     v[5] = ds * (ubyte_f32<1>(q1) - 32.0f);
     v[6] = ds * (ubyte_f32<2>(q1) - 32.0f);
     v[7] = ds * (ubyte_f32<3>(q1) - 32.0f);
-    store8(out + (size_t)row * ld + kb * 256 + e0, v);
 }
 
-// Q8_0: 32 elements, value d·q.
-__global__ __launch_bounds__(kThreads) void dequant_q80(const uint8_t *__restrict__ wq,
-                                                        uint16_t *__restrict__ out, uint32_t nb,
-                                                        uint32_t K, uint32_t ld, uint32_t n_data,
-                                                        uint32_t pad_per_row, uint32_t n_total) {
-    const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
-    if (u >= n_total) return;
-    if (u >= n_data) {
-        write_pad(out, u - n_data, pad_per_row, K, ld);
+// Q8_0, 8 outputs e0..e0+7 of the block at `blk` (2-byte aligned): value d·q.
+__device__ __forceinline__ void decode_q80(const uint8_t *blk, uint32_t e0, float v[8]) {
+    const float d = f16_bits_to_f32(lds_u16(blk));
+    const uint32_t q0 = lds_u32_a2(blk + 2 + e0), q1 = lds_u32_a2(blk + 6 + e0);
+    v[0] = d * sbyte_f32<0>(q0);
+    v[1] = d * sbyte_f32<1>(q0);
+    v[2] = d * sbyte_f32<2>(q0);
+    v[3] = d * sbyte_f32<3>(q0);
+    v[4] = d * sbyte_f32<0>(q1);
+    v[5] = d * sbyte_f32<1>(q1);
+    v[6] = d * sbyte_f32<2>(q1);
+    v[7] = d * sbyte_f32<3>(q1);
+}
+
+// One workgroup decodes group_blocks<FMT>() consecutive blocks (16 KiB of f16
+// output).  Phase 1: the blocks' bytes — a contiguous span of the weight —
+// are staged in LDS with 16-byte loads from its 16-byte-aligned cover (a
+// 16-byte chunk that holds a wanted byte lies on that byte's page, so no
+// load can fault).  Phase 2: each thread decodes kChunksPerThread runs of 8
+// outputs, run u = first + i·256 + thread, so every store instruction of a
+// wave writes 1 KiB of contiguous cache row.  Workgroups past the data write
+// the +0 pad columns [K, ld).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ wq,
+                                                           uint16_t *__restrict__ out, uint32_t nb,
+                                                           uint32_t K, uint32_t ld,
+                                                           uint32_t n_blocks, uint32_t data_groups,
+                                                           uint32_t pad_per_row, uint32_t n_pad) {
+    constexpr uint32_t BE = Fmt<FMT>::BE, BB = Fmt<FMT>::BB, G = group_blocks<FMT>();
+    constexpr uint32_t CPB = BE / 8;   // output runs per block
+    __shared__ u32x4 stage[stage_bytes<FMT>() / 16];
+    const uint32_t tid = threadIdx.x;
+
+    if (blockIdx.x >= data_groups) {   // pad columns
+        const uint32_t p0 = (blockIdx.x - data_groups) * kChunksPerGroup;
+#pragma unroll
+        for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+            const uint32_t p = p0 + i * kThreads + tid;
+            if (p < n_pad) {
+                const uint32_t row = p / pad_per_row, c = p - row * pad_per_row;
+                *(u32x4 *)(out + (size_t)row * ld + K + 8 * c) = u32x4{0, 0, 0, 0};
+            }
+        }
         return;
     }
-    const uint32_t g = u >> 2, p = u & 3;
-    const uint32_t row = g / nb, kb = g - row * nb;
-    const uint8_t *blk = wq + (size_t)g * 34;
-    const float d = f16_bits_to_f32(*(const uint16_t *)blk);
-    const u32x2 q = load8_a2(blk + 2 + 8 * p);
-    float v[8];
-    v[0] = d * sbyte_f32<0>(q.x);
-    v[1] = d * sbyte_f32<1>(q.x);
-    v[2] = d * sbyte_f32<2>(q.x);
-    v[3] = d * sbyte_f32<3>(q.x);
-    v[4] = d * sbyte_f32<0>(q.y);
-    v[5] = d * sbyte_f32<1>(q.y);
-    v[6] = d * sbyte_f32<2>(q.y);
-    v[7] = d * sbyte_f32<3>(q.y);
-    store8(out + (size_t)row * ld + kb * 32 + 8 * p, v);
+
+    const uint32_t g0 = blockIdx.x * G;
+    const uint32_t gcount = min(G, n_blocks - g0);
+    const size_t begin = (size_t)g0 * BB, end = begin + (size_t)gcount * BB;
+    const size_t abegin = begin & ~(size_t)15;
+    const uint32_t lead = (uint32_t)(begin - abegin);
+    const uint32_t nchunks = (uint32_t)((end - abegin + 15) >> 4);
+    const u32x4 *src = (const u32x4 *)(wq + abegin);
+    constexpr uint32_t kLoads = (stage_bytes<FMT>() / 16 + kThreads - 1) / kThreads;
+    u32x4 tmp[kLoads];
+#pragma unroll
+    for (uint32_t i = 0; i < kLoads; ++i) {
+        const uint32_t c = i * kThreads + tid;
+        if (c < nchunks) tmp[i] = src[c];
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < kLoads; ++i) {
+        const uint32_t c = i * kThreads + tid;
+        if (c < nchunks) stage[c] = tmp[i];
+    }
+    __syncthreads();
+
+    const uint8_t *bytes = (const uint8_t *)stage + lead;
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t u = i * kThreads + tid;          // run within the group
+        const uint32_t gl = u / CPB;                    // block within the group
+        if (gl >= gcount) break;
+        const uint32_t e0 = (u - gl * CPB) * 8;
+        const uint32_t g = g0 + gl;
+        const uint32_t row = g / nb, kb = g - row * nb;
+        float v[8];
+        if constexpr (FMT == kFmtQ4_K) decode_q4k(bytes + gl * BB, e0, v);
+        else if constexpr (FMT == kFmtQ6_K) decode_q6k(bytes + gl * BB, e0, v);
+        else decode_q80(bytes + gl * BB, e0, v);
+        store8(out + (size_t)row * ld + kb * BE + e0, v);
+    }
+}
+
+template <int FMT>
+hipError_t launch(const void *wq, int N, int K, uint16_t *w16, int ld, hipStream_t stream) {
+    constexpr uint32_t G = group_blocks<FMT>();
+    const uint32_t nb = (uint32_t)K / Fmt<FMT>::BE;
+    const uint32_t n_blocks = (uint32_t)N * nb;
+    const uint32_t data_groups = (n_blocks + G - 1) / G;
+    const uint32_t pad_per_row = (uint32_t)(ld - K) / 8;
+    const uint32_t n_pad = (uint32_t)N * pad_per_row;
+    const uint32_t pad_groups = (n_pad + kChunksPerGroup - 1) / kChunksPerGroup;
+    hipLaunchKernelGGL(dequant_kernel<FMT>, dim3(data_groups + pad_groups), dim3(kThreads), 0,
+                       stream, (const uint8_t *)wq, w16, nb, (uint32_t)K, (uint32_t)ld, n_blocks,
+                       data_groups, pad_per_row, n_pad);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_dequant(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
                           hipStream_t stream) {
-    const uint32_t be = (uint32_t)block_elems(fmt);
-    const uint32_t nb = (uint32_t)K / be;
-    const uint32_t n_data = (uint32_t)((uint64_t)N * (uint32_t)K / 8);
-    const uint32_t pad_per_row = (uint32_t)(ld - K) / 8;
-    const uint32_t n_total = n_data + (uint32_t)N * pad_per_row;
-    const dim3 grid((n_total + kThreads - 1) / kThreads), block(kThreads);
-    const uint8_t *q = (const uint8_t *)wq;
     switch (fmt) {
-    case kFmtQ4_K:
-        hipLaunchKernelGGL(dequant_q4k, grid, block, 0, stream, q, w16, nb, (uint32_t)K,
-                           (uint32_t)ld, n_data, pad_per_row, n_total);
-        break;
-    case kFmtQ6_K:
-        hipLaunchKernelGGL(dequant_q6k, grid, block, 0, stream, q, w16, nb, (uint32_t)K,
-                           (uint32_t)ld, n_data, pad_per_row, n_total);
-        break;
-    default:
-        hipLaunchKernelGGL(dequant_q80, grid, block, 0, stream, q, w16, nb, (uint32_t)K,
-                           (uint32_t)ld, n_data, pad_per_row, n_total);
-        break;
+    case kFmtQ4_K: return launch<kFmtQ4_K>(wq, N, K, w16, ld, stream);
+    case kFmtQ6_K: return launch<kFmtQ6_K>(wq, N, K, w16, ld, stream);
+    default: return launch<kFmtQ8_0>(wq, N, K, w16, ld, stream);
     }
-    return hipGetLastError();
 }
 
 }  // namespace mq
