@@ -78,23 +78,30 @@ def make_weights(torch, mq, layers, dev):
 
 
 def load_phase(torch, mq, W, reps):
-    """Decode every weight into its cache; per-call HIP-event times (ms)."""
+    """Decode every weight into its cache, back to back as a model load does.
+
+    Returns (best total ms over `reps` timed loads, per-call records of one
+    extra instrumented load with HIP events around each call)."""
+    calls = [(name, fmt, N, K, q, cache) for row in W for name, (fmt, N, K, q, cache) in row.items()]
     best = None
     for _ in range(reps):
-        evs = []
-        for row in W:
-            for name, (fmt, N, K, q, cache) in row.items():
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                mq.dequant_to_f16(q, fmt, N, K, out=cache)
-                b.record()
-                evs.append((name, fmt, N, K, q.numel(), a, b))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for name, fmt, N, K, q, cache in calls:
+            mq.dequant_to_f16(q, fmt, N, K, out=cache)
+        b.record()
         torch.cuda.synchronize()
-        rec = [(name, fmt, N, K, qb, a.elapsed_time(b)) for name, fmt, N, K, qb, a, b in evs]
-        tot = sum(r[-1] for r in rec)
-        if best is None or tot < best[0]:
-            best = (tot, rec)
-    return best[1]
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    evs = []
+    for name, fmt, N, K, q, cache in calls:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        mq.dequant_to_f16(q, fmt, N, K, out=cache)
+        b.record()
+        evs.append((name, fmt, N, K, q.numel(), a, b))
+    torch.cuda.synchronize()
+    return best, [(name, fmt, N, K, qb, a.elapsed_time(b)) for name, fmt, N, K, qb, a, b in evs]
 
 
 def forward(mq, W, xa, xf, ys, ws, events=None):
@@ -235,8 +242,7 @@ def main():
     cbytes = sum(r[n][1] * r[n][2] * 2 for r in W for n in r)
     log(f"[bench] {layers * 7} weights drawn on device in {time.time() - t0:.1f}s: "
         f"{qbytes / 1e9:.3f} GB quantized, {cbytes / 1e9:.3f} GB f16")
-    rec = load_phase(torch, mq, W, args.load_reps)
-    deq_ms = sum(r[-1] for r in rec)
+    deq_ms, rec = load_phase(torch, mq, W, args.load_reps)
     deq_gbs = (qbytes + cbytes) / (deq_ms / 1e3) / 1e9
     per_fmt = {}
     for name, fmt, N, K, qb, ms in rec:
@@ -246,6 +252,14 @@ def main():
     log(f"[bench] load phase: {deq_ms:.2f} ms for {len(rec)} dequants, {deq_gbs:.0f} GB/s "
         f"({100 * deq_gbs / PEAK_HBM_GBS:.1f}% of HBM peak); " +
         ", ".join(f"{k} {v[0] / v[1] / 1e6:.0f} GB/s" for k, v in per_fmt.items()))
+    per_mat = {}
+    for name, fmt, N, K, qb, ms in rec:
+        m = per_mat.setdefault(name, [0, 0.0, 0])
+        m[0] += qb + 2 * N * K
+        m[1] += ms
+        m[2] += 1
+    log("    per matrix (instrumented pass): " + ", ".join(f"{n} {v[1] / v[2] * 1e3:.1f} us {v[0] / v[1] / 1e6:.0f} GB/s"
+                                       for n, v in per_mat.items()))
 
     # -- the timed forward --------------------------------------------------------
     xa = synth.activations_device(7001, M, 3584, dev)

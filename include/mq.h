@@ -107,11 +107,14 @@ int64_t mq_f16cache_ld(int64_t K);
 int mq_dequant_to_f16(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
                       void *stream);
 
-/* Workspace bytes the GEMM entry points need for this problem: 0 when the
- * launch is not split along K, else split_k · M · N · 4 (one f32 partial plane
- * per split, reduced in a fixed order so results are deterministic; Fucina
- * "Eager GPU Offload Without A Compute Graph", F16/quantized linears: split-K
- * for underfilled grids with caller-owned partial planes).
+/* Workspace bytes the GEMM entry points need for this problem: 0 when no
+ * tile is split along K, else split · T · BM · BN · 4 for the T tiles that
+ * are split (one f32 partial tile per K range, summed in a fixed order so
+ * results are deterministic; Fucina "Eager GPU Offload Without A Compute
+ * Graph", F16/quantized linears: split-K where the output grid underfills the
+ * device, with caller-owned partials).  With split_k = 0 the library runs
+ * whole rounds of 256 tiles over all of K and splits only the tiles of a last,
+ * partial round; a forced split_k >= 2 splits every tile.
  *   fmt     : 0 for mq_gemm_f16cache, else the weight format of mq_gemm_fused.
  *   split_k : 0 = let the library choose (as the GEMM will with the same
  *             arguments), 1 = no split, 2..MQ_MAX_SPLIT_K = forced.

@@ -22,14 +22,19 @@ inline int block_bytes(int fmt) {
 hipError_t launch_dequant(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
                           hipStream_t stream);
 
-// Launch shape of one GEMM: tile sizes, K split and workspace.
+// Launch shape of one GEMM.  Tiles are numbered in raster order; the first
+// dp_tiles run over all of K and write Y directly, the remaining tail_tiles
+// are each split into `split` K ranges whose f32 partial tiles go to the
+// workspace and are summed in a fixed order by a second kernel.
 struct GemmPlan {
     int bm, bn;             // block tile (M rows of X, N rows of W)
     int tiles_m, tiles_n;
     int k_steps;            // ceil(K / 64)
-    int split;              // number of K partitions actually launched (>= 1)
-    int steps_per_split;    // k-steps per partition
-    int64_t ws_bytes;       // split > 1: split * M * N * 4, else 0
+    int dp_tiles;           // tiles computed over the whole K
+    int tail_tiles;         // tiles split along K (0 when split == 1)
+    int split;              // K ranges per tail tile (>= 1)
+    int steps_per_split;    // k-steps per range
+    int64_t ws_bytes;       // split · tail_tiles · bm · bn · 4, or 0
 };
 
 // split_req: 0 = choose, 1..16 = requested partitions (clamped to the k-steps).

@@ -85,6 +85,24 @@ def test_forced_split_integer_exact(split):
     assert np.array_equal(Y.astype(np.float64), Yref)
 
 
+def test_mixed_grid_tail_split_integer_exact():
+    """One launch with both kinds of workgroup: M = 2048, N = 8448 gives 8 x 33 =
+    264 tiles of 256 x 256, i.e. one whole round of 256 tiles over all of K and 8
+    tail tiles split along K (their partials summed by the reduce kernel).  With
+    integer inputs every partial sum is exact, so Y must equal the oracle on
+    rows that cross both the whole tiles and the tail tiles."""
+    M, N, K = 2048, 8448, 2048
+    ws = mq.workspace_bytes(0, M, N, K)
+    assert ws > 0 and ws % (256 * 256 * 4 * 8) == 0   # split * 8 tail tiles
+    x = synth.activations(synth.rng(24, role=1), M, K, mode="integer")
+    _, w16 = _cache(12, N, K, 24, mode="integer")
+    Y, _ = _gemm(x, w16, K)
+    rows = np.unique(np.concatenate([[0, 255, 1023, 1024, 2047],
+                                     np.random.default_rng(24).choice(M, 40)]))
+    Yref, _ = oracle.gemm_ref(x[rows], w16, K)
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
+
+
 def test_onehot_reproduces_cache():
     _, w16 = _cache(14, 384, 512, 13)
     x = synth.activations(None, 512, 512, mode="onehot")
