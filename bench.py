@@ -36,7 +36,17 @@ import synth  # noqa: E402
 METRIC = "prefill GEMM TFLOP/s + matmul tok/s (7B Q4_K, M=2048); dequant GB/s"
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense f16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-ROOFLINE_KERNEL = "gemm_kernel<256, 128, f16 cache, full-K>"
+# The dominant kernel of the step: the gate and up GEMMs (2 x 28 of the 196
+# calls, ~60% of the matmul time), i.e. gemm_kernel<256, 256, f16> plus the
+# fixed-order reduce of its K-split tail tiles (one mq_gemm_f16cache call).
+ROOFLINE_SHAPES = ("gate", "up")
+ROOFLINE_KERNEL = "gemm_kernel<256, 256, f16> + splitk_reduce (mq_gemm_f16cache, gate/up 18944x3584)"
+# Measured HBM traffic of that call (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
+# by a plain copy of known size) with the hash of the GEMM source it was taken
+# on; reported only while the source is unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_f16cache_gate_7b_m2048_traffic.md")
+GEMM_SOURCES = ("quantized_weight_prefill_q4_amd/csrc/gemm.hip",
+                "quantized_weight_prefill_q4_amd/csrc/mq_device.h")
 
 
 def log(*a):
@@ -54,9 +64,73 @@ def parse():
     p.add_argument("--fused-steps", type=int, default=5)
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=128,
+    p.add_argument("--cpu-rows", type=int, default=2048,
                    help="token rows of the oracle sample (one layer's 7 matrices)")
+    p.add_argument("--only-shape", default=None,
+                   help="profiling aid: run only this 7B matrix's cache GEMM --steps times")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="profiling aid: run only a plain 1 GiB device copy --steps times "
+                        "(the reference for the HBM byte counters)")
     return p.parse_args()
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """(bytes per call, note) from the committed counter summary, or (None, why)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None, "no counter summary"
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_call:") or line.startswith("source_sha256_16:"):
+            k, v = line.split(":", 1)
+            vals[k] = v.strip()
+    if vals.get("source_sha256_16") != gemm_source_hash():
+        return None, "GEMM source changed since the counters were taken"
+    return int(vals["traffic_bytes_per_call"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
+def run_only_shape(torch, mq, name, steps, dev):
+    fmt, N, K = next((f, n, k) for nm, f, n, k in synth.LAYER_7B if nm == name)
+    M = 2048
+    q = synth.weights_device(fmt, 1, N, K, dev)
+    cache = mq.dequant_to_f16(q, fmt, N, K)
+    x = synth.activations_device(2, M, K, dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws_n = mq.workspace_bytes(0, M, N, K)
+    ws = torch.empty(max(1, ws_n // 4), dtype=torch.float32, device=dev)
+    mq.gemm_f16cache(x, cache, K, out=y, ws=ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record()
+        mq.gemm_f16cache(x, cache, K, out=y, ws=ws)
+    ev[steps].record()
+    torch.cuda.synchronize()
+    us = statistics.median(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+    print(json.dumps({"only_shape": name, "M": M, "N": N, "K": K, "calls": steps + 1,
+                      "median_call_us": round(us, 2),
+                      "tflops": round(2.0 * M * N * K / us / 1e6, 1),
+                      "algorithmic_bytes_per_call": M * K * 2 + N * K * 2 + M * N * 4}), flush=True)
+
+
+def run_calib_copy(torch, steps, dev):
+    n = 1 << 28   # 2^28 f32 = 1 GiB read + 1 GiB written per copy
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n,
+                      "copies": steps}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -232,6 +306,12 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calib_copy:
+        run_calib_copy(torch, args.steps, dev)
+        return
+    if args.only_shape:
+        run_only_shape(torch, mq, args.only_shape, args.steps, dev)
+        return
     M, layers = args.M, args.layers
     log(f"[bench] device {torch.cuda.get_device_name(0)}, library {mq.LIB_PATH}")
 
@@ -287,16 +367,15 @@ def main():
                          for e in steps_events])
     med_call = np.median(per_call, axis=0)
     flops = np.array([2.0 * M * N * K for _, _, N, K in calls])
-    shape_rows, full_k = [], []
+    shape_rows = []
     for n, f, N, K in synth.LAYER_7B:
         idx = [i for i, c in enumerate(calls) if c[0] == n]
         t_us = float(med_call[idx].mean() * 1e3)
         shape_rows.append((n, N, K, t_us, 2.0 * M * N * K / t_us / 1e6))
-        if mq.workspace_bytes(0, M, N, K) == 0:
-            full_k += idx
-    full_k = np.array(sorted(full_k))
-    ach = float(flops[full_k].sum() / (per_call[:, full_k].sum(axis=1).mean() / 1e3) / 1e12)
-    avg_launch_us = float(per_call[:, full_k].mean() * 1e3)
+    dom = np.array([i for i, c in enumerate(calls) if c[0] in ROOFLINE_SHAPES])
+    ach = float(flops[dom].sum() / (per_call[:, dom].sum(axis=1).mean() / 1e3) / 1e12)
+    avg_launch_us = float(per_call[:, dom].mean() * 1e3)
+    traffic, traffic_note = measured_traffic()
     gemm_tflops = float(flops.sum() / (ev_step_ms / 1e3) / 1e12)
     tok_s = M * args.steps / wall
     log(f"[bench] forward: {ms_per_step:.3f} ms/step wall, {ev_step_ms:.3f} ms in events, "
@@ -304,9 +383,9 @@ def main():
     for n, N, K, t_us, tf in shape_rows:
         log(f"    {n:5s} {N:6d}x{K:<6d} {t_us:9.1f} us  {tf:7.1f} TFLOP/s  "
             f"({100 * tf / PEAK_F16_TFLOPS:.1f}% of peak)")
-    log(f"[bench] roofline kernel ({ROOFLINE_KERNEL}, {len(full_k)} launches/step): "
+    log(f"[bench] roofline kernel ({ROOFLINE_KERNEL}, {len(dom)} calls/step): "
         f"{ach:.0f} TFLOP/s = {100 * ach / PEAK_F16_TFLOPS:.1f}% of {PEAK_F16_TFLOPS:.0f}, "
-        f"avg launch {avg_launch_us:.1f} us")
+        f"avg call {avg_launch_us:.1f} us; traffic {traffic} B/call ({traffic_note})")
 
     # -- fused forward (no cache) ---------------------------------------------------
     fused = None
@@ -370,9 +449,11 @@ def main():
         "per_shape_tflops": {n: round(tf, 1) for n, _, _, _, tf in shape_rows},
         "roofline": {
             "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_F16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+            "traffic_note": traffic_note,
             "kernel": ROOFLINE_KERNEL, "avg_launch_us": round(avg_launch_us, 2),
-            "launches_per_step": int(len(full_k)),
+            "launches_per_step": int(len(dom)),
+            "algorithmic_bytes_per_call": M * 3584 * 2 + 18944 * 3584 * 2 + M * 18944 * 4,
         },
         "dequant_roofline": {
             "bound": "hbm", "achieved": round(deq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
