@@ -107,6 +107,28 @@ int64_t mq_f16cache_ld(int64_t K);
 int mq_dequant_to_f16(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
                       void *stream);
 
+/* One weight of a batched decode (see mq_dequant_to_f16_batch); the fields
+ * mean what the same-named arguments of mq_dequant_to_f16 mean. */
+typedef struct mq_dequant_job {
+    int fmt;             /* MQ_Q4_K, MQ_Q6_K or MQ_Q8_0 */
+    int N, K;            /* rows; columns, a multiple of the format's block */
+    int ld;              /* cache row stride in halves: >= K, multiple of 8 */
+    const void *wq;      /* device, 16-byte aligned, N·mq_row_bytes(fmt, K) bytes */
+    uint16_t *w16;       /* device, 16-byte aligned, N·ld halves */
+} mq_dequant_job;
+
+/* The load-time decode of several weights at once: for each jobs[i], exactly
+ * what mq_dequant_to_f16 would write (minfer 05 · 8p §2: every weight is
+ * decoded once, when the model is loaded; the decodes are independent).  The
+ * jobs are packed, up to 16 per kernel launch, into the launch arguments, so
+ * small matrices share a launch instead of each ramping the GPU up and down.
+ *   jobs : HOST array of n descriptors, read during the call only.
+ *   n    : number of jobs; 0 is a no-op.
+ * Every job is checked before anything is enqueued: the first invalid job's
+ * MQ_ERR_* code is returned and nothing runs.  Jobs must not overlap in w16;
+ * they run in no particular order relative to each other, all on `stream`. */
+int mq_dequant_to_f16_batch(const mq_dequant_job *jobs, int n, void *stream);
+
 /* Workspace bytes the GEMM entry points need for this problem: 0 when no
  * tile is split along K, else split · T · BM · BN · 4 for the T tiles that
  * are split (one f32 partial tile per K range, summed in a fixed order so

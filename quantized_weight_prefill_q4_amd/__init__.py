@@ -19,6 +19,7 @@ from .api import (
     block_elems,
     cache_ld,
     dequant_to_f16,
+    dequant_to_f16_batch,
     gemm_f16cache,
     gemm_fused,
     row_bytes,
@@ -36,6 +37,7 @@ __all__ = [
     "block_elems",
     "cache_ld",
     "dequant_to_f16",
+    "dequant_to_f16_batch",
     "gemm_f16cache",
     "gemm_fused",
     "lib",

@@ -26,6 +26,14 @@ MQ_Q6_K = 14
 
 _c_int, _c_i64, _c_size, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
+
+
+class MqDequantJob(ctypes.Structure):
+    """struct mq_dequant_job of include/mq.h."""
+    _fields_ = [("fmt", _c_int), ("N", _c_int), ("K", _c_int), ("ld", _c_int),
+                ("wq", _vp), ("w16", _vp)]
+
+
 # name -> (restype, argtypes); mirrors include/mq.h
 SIGNATURES = {
     "mq_block_elems": (_c_int, [_c_int]),
@@ -33,6 +41,7 @@ SIGNATURES = {
     "mq_row_bytes": (_c_i64, [_c_int, _c_i64]),
     "mq_f16cache_ld": (_c_i64, [_c_i64]),
     "mq_dequant_to_f16": (_c_int, [_c_int, _vp, _c_int, _c_int, _vp, _c_int, _vp]),
+    "mq_dequant_to_f16_batch": (_c_int, [ctypes.POINTER(MqDequantJob), _c_int, _vp]),
     "mq_gemm_workspace_bytes": (_c_i64, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "mq_gemm_f16cache": (_c_int, [_vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int,
                                   _vp, _c_size, _c_int, _vp]),

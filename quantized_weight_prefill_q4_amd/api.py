@@ -10,7 +10,9 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import MQ_Q4_K, MQ_Q6_K, MQ_Q8_0, check, lib
+import ctypes
+
+from ._lib import MQ_Q4_K, MQ_Q6_K, MQ_Q8_0, MqDequantJob, check, lib
 
 FORMATS = {"q8_0": MQ_Q8_0, "q4_k": MQ_Q4_K, "q6_k": MQ_Q6_K}
 
@@ -76,6 +78,34 @@ def dequant_to_f16(wq: torch.Tensor, fmt, N: int, K: int, pad: bool = True,
     check(lib().mq_dequant_to_f16(f, wq.data_ptr(), N, K, out.data_ptr(), ld, _stream(wq)),
           "mq_dequant_to_f16")
     return out
+
+
+def dequant_to_f16_batch(jobs, pad: bool = True) -> list[torch.Tensor]:
+    """Decode several weights with one library call (launches of up to 16
+    jobs each).  ``jobs``: iterable of ``(wq, fmt, N, K)`` or ``(wq, fmt, N, K,
+    out)``; returns the caches in order, each as ``dequant_to_f16`` would."""
+    jobs = list(jobs)
+    arr = (MqDequantJob * max(1, len(jobs)))()
+    outs = []
+    stream = None
+    for i, job in enumerate(jobs):
+        wq, fmt, N, K = job[:4]
+        out = job[4] if len(job) > 4 else None
+        _need_cuda(wq, "wq", torch.uint8)
+        if not wq.is_contiguous():
+            raise ValueError("wq must be contiguous")
+        ld = cache_ld(K) if pad else K
+        if out is None:
+            out = torch.empty((N, ld), dtype=torch.float16, device=wq.device)
+        else:
+            _need_cuda(out, "out", torch.float16)
+            ld = _row_major_2d(out, "out")
+        if stream is None:
+            stream = _stream(wq)
+        arr[i] = MqDequantJob(_fmt(fmt), N, K, ld, wq.data_ptr(), out.data_ptr())
+        outs.append(out)
+    check(lib().mq_dequant_to_f16_batch(arr, len(jobs), stream), "mq_dequant_to_f16_batch")
+    return outs
 
 
 def _workspace(fmt_code: int, M: int, N: int, K: int, split_k: int, device) -> torch.Tensor | None:

@@ -31,6 +31,17 @@ int hip_status(hipError_t e) {
     return MQ_ERR_HIP;
 }
 
+// Checks of one decode (mq_dequant_to_f16 and each job of a batch).
+int check_dequant(int fmt, const void *wq, int N, int K, const uint16_t *w16, int ld) {
+    if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    if (!wq || !w16) return MQ_ERR_NULL;
+    if (check_dims(1, N, K) || K % mq::block_elems(fmt)) return MQ_ERR_SHAPE;
+    if (!ld_ok(ld, K)) return MQ_ERR_LD;
+    if (!aligned16(wq) || !aligned16(w16)) return MQ_ERR_ALIGN;
+    if ((int64_t)N * ld / 8 >= ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
+    return MQ_OK;
+}
+
 // Shared checks of both GEMM entry points; fills the plan on success.
 int check_gemm(int fmt, const void *X, int ldx, const void *W, int64_t ldw_elems, const float *Y,
                int ldy, int M, int N, int K, const void *ws, size_t ws_bytes, int split_k,
@@ -80,13 +91,29 @@ int64_t mq_f16cache_ld(int64_t K) {
 
 int mq_dequant_to_f16(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
                       void *stream) {
-    if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
-    if (!wq || !w16) return MQ_ERR_NULL;
-    if (check_dims(1, N, K) || K % mq::block_elems(fmt)) return MQ_ERR_SHAPE;
-    if (!ld_ok(ld, K)) return MQ_ERR_LD;
-    if (!aligned16(wq) || !aligned16(w16)) return MQ_ERR_ALIGN;
-    if ((int64_t)N * ld / 8 >= ((int64_t)1 << 31)) return MQ_ERR_SHAPE;
+    if (int rc = check_dequant(fmt, wq, N, K, w16, ld)) return rc;
     return hip_status(mq::launch_dequant(fmt, wq, N, K, w16, ld, (hipStream_t)stream));
+}
+
+int mq_dequant_to_f16_batch(const mq_dequant_job *jobs, int n, void *stream) {
+    if (n < 0) return MQ_ERR_SHAPE;
+    if (n == 0) return MQ_OK;
+    if (!jobs) return MQ_ERR_NULL;
+    for (int i = 0; i < n; ++i) {
+        const mq_dequant_job &j = jobs[i];
+        if (int rc = check_dequant(j.fmt, j.wq, j.N, j.K, j.w16, j.ld)) return rc;
+    }
+    constexpr int kChunk = 64;
+    mq::DequantSpec specs[kChunk];
+    for (int first = 0; first < n; first += kChunk) {
+        const int m = n - first < kChunk ? n - first : kChunk;
+        for (int i = 0; i < m; ++i) {
+            const mq_dequant_job &j = jobs[first + i];
+            specs[i] = mq::DequantSpec{j.fmt, j.N, j.K, j.ld, j.wq, j.w16};
+        }
+        if (int rc = hip_status(mq::launch_dequant_batch(specs, m, (hipStream_t)stream))) return rc;
+    }
+    return MQ_OK;
 }
 
 int64_t mq_gemm_workspace_bytes(int fmt, int M, int N, int K, int split_k) {

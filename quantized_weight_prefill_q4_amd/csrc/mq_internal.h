@@ -22,6 +22,15 @@ inline int block_bytes(int fmt) {
 hipError_t launch_dequant(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
                           hipStream_t stream);
 
+// One decode of a batch (arguments already validated).
+struct DequantSpec {
+    int fmt, N, K, ld;
+    const void *wq;
+    uint16_t *w16;
+};
+// Decodes specs[0..n) in launches of up to 16 jobs, in order, on `stream`.
+hipError_t launch_dequant_batch(const DequantSpec *specs, int n, hipStream_t stream);
+
 // Launch shape of one GEMM.  Tiles are numbered in raster order; the first
 // dp_tiles run over all of K and write Y directly, the remaining tail_tiles
 // are each split into `split` K ranges whose f32 partial tiles go to the

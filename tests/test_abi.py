@@ -114,6 +114,25 @@ def test_fused_rejects(L):
     assert f(12, FAKE, 512, FAKE, FAKE, 256, 64, 256, 512, None, 0, 4, None) == _lib.MQ_ERR_WORKSPACE
 
 
+def test_dequant_batch_rejects(L):
+    J = _lib.MqDequantJob
+    ok = J(12, 64, 256, 256, FAKE, FAKE)
+    f = L.mq_dequant_to_f16_batch
+    assert f(None, 0, None) == _lib.MQ_OK            # empty batch: no-op
+    assert f(None, 2, None) == _lib.MQ_ERR_NULL
+    assert f((J * 1)(ok), -1, None) == _lib.MQ_ERR_SHAPE
+    # the first invalid job's code is returned and nothing is launched (a
+    # launch without a GPU would report MQ_ERR_HIP instead)
+    for bad, code in ((J(5, 64, 256, 256, FAKE, FAKE), _lib.MQ_ERR_FORMAT),
+                      (J(12, 64, 100, 256, FAKE, FAKE), _lib.MQ_ERR_SHAPE),
+                      (J(12, 64, 256, 200, FAKE, FAKE), _lib.MQ_ERR_LD),
+                      (J(12, 64, 256, 256, MIS, FAKE), _lib.MQ_ERR_ALIGN),
+                      (J(14, 64, 256, 256, FAKE, None), _lib.MQ_ERR_NULL),
+                      (J(8, 0, 32, 32, FAKE, FAKE), _lib.MQ_ERR_SHAPE)):
+        arr = (J * 3)(ok, ok, bad)
+        assert f(arr, 3, None) == code
+
+
 def test_workspace_planning(L):
     # k/v projection at M=2048 underfills 256 CUs with 256x128 tiles -> split
     ws = L.mq_gemm_workspace_bytes(12, 2048, 512, 3584, 0)

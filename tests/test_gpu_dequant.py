@@ -118,3 +118,52 @@ REAL = [
 def test_real_shapes_full(name, fmt, N, K):
     q = synth.weights(fmt, synth.rng(5, 0, N % 97, K % 89), N, K)
     _check(fmt, q, N, K, pad=True, what=name)
+
+
+def test_batch_matches_oracle_across_launches():
+    """mq_dequant_to_f16_batch: 21 jobs of all three formats, padded and
+    unpadded, odd row counts — two kernel launches (16 + 5 jobs) with
+    workgroups of different jobs and formats in one grid.  Every cache must
+    equal the oracle's bit for bit, pad columns +0."""
+    shapes = [(12, 3, 256), (14, 5, 512), (8, 7, 96), (12, 130, 2048), (14, 65, 1024),
+              (8, 300, 4096), (12, 1, 4096), (14, 2, 256), (8, 33, 32), (12, 17, 3584)]
+    jobs, exp = [], []
+    for i in range(21):
+        fmt, N, K = shapes[i % len(shapes)]
+        pad = i % 3 != 1
+        q = synth.weights(fmt, synth.rng(40, 0, fmt, i), N, K)
+        jobs.append((to_dev_u8(q), fmt, N, K))
+        exp.append((fmt, N, K, pad, oracle.cache_ref(fmt, q, N, K, pad=pad)))
+    announce("dequant_batch", f"{len(jobs)} jobs")
+    outs = [None] * len(jobs)
+    for pad in (True, False):
+        idx = [i for i, e in enumerate(exp) if e[3] == pad]
+        res = mq.dequant_to_f16_batch([jobs[i] for i in idx], pad=pad)
+        for i, r in zip(idx, res):
+            outs[i] = r
+    for (fmt, N, K, pad, e), o in zip(exp, outs):
+        got = f16_bits(o)
+        assert got.shape == e.shape
+        assert_bits_equal(got, e, f"batch {FMT_NAME[fmt]} {N}x{K} pad={pad}")
+
+
+def test_batch_of_7b_layer_equals_single_calls():
+    """The load phase's use: one layer's 7 weights (q, k, v, o, gate, up in Q4_K,
+    down in Q6_K) decoded by one batched call equal the single-call caches bit
+    for bit, plus more than 64 jobs (the library's host-side chunk) of a small
+    matrix."""
+    jobs, singles = [], []
+    for mi, (name, fmt, N, K) in enumerate(synth.LAYER_7B):
+        q = to_dev_u8(synth.weights(fmt, synth.rng(41, 0, mi, 0), N, K))
+        jobs.append((q, fmt, N, K))
+        announce("dequant", name, f"N={N}", f"K={K}")
+        singles.append(f16_bits(mq.dequant_to_f16(q, fmt, N, K)))
+    announce("dequant_batch", "7B layer")
+    for got, exp in zip(mq.dequant_to_f16_batch(jobs), singles):
+        assert np.array_equal(f16_bits(got), exp)
+    q = synth.weights(8, synth.rng(42, 0, 8, 0), 9, 64)
+    exp = oracle.cache_ref(8, q, 9, 64, pad=True)
+    dq = to_dev_u8(q)
+    announce("dequant_batch", "70 jobs")
+    for o in mq.dequant_to_f16_batch([(dq, 8, 9, 64)] * 70):
+        assert_bits_equal(f16_bits(o), exp, "batch of 70")
