@@ -647,7 +647,7 @@ hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
 
 template <int FMT>
 hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t stream) {
-    if constexpr (FMT == kFmtF16)
+    if constexpr (FMT != kFmtQ6_K)
         if (bn == 256) return launch_tile<256, 256, FMT>(a, grid, stream);
     switch (bm) {
     case 64: return launch_tile<64, 128, FMT>(a, grid, stream);
@@ -662,9 +662,11 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req) {
     GemmPlan p;
     p.bn = 128;
     p.bm = M > 128 ? 256 : (M > 64 ? 128 : 64);
-    // f16 operands with a full wave of 256 × 256 tiles take the larger tile:
-    // half the operand bytes per flop through L2 and LDS.
-    if (fmt == kFmtF16 && M > 128 && (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= kCUs)
+    // With at least one full round of 256 × 256 tiles the larger tile is used
+    // (half the operand bytes per flop through L2 and LDS): for the f16 cache
+    // and the Q4_K / Q8_0 fused kernels; Q6_K's raw-byte registers do not fit
+    // beside 256 accumulators.
+    if (fmt != kFmtQ6_K && M > 128 && (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= kCUs)
         p.bn = 256;
     p.tiles_m = (M + p.bm - 1) / p.bm;
     p.tiles_n = (N + p.bn - 1) / p.bn;

@@ -141,8 +141,10 @@ def test_workspace_planning(L):
     # gate/up: 8 x 74 tiles of 256 x 256 = two full rounds of 256 plus 80 tiles,
     # which are split 256 // 80 = 3 ways along K
     assert L.mq_gemm_workspace_bytes(0, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
-    # the fused kernel's 256 x 128 tiles: 4 rounds + 160 tiles -> no split
-    assert L.mq_gemm_workspace_bytes(12, 2048, 18944, 3584, 0) == 0
+    # the Q4_K fused kernel uses the same tiles (same plan); Q6_K keeps 256 x 128
+    # tiles: 4 rounds + 160 tiles -> no split
+    assert L.mq_gemm_workspace_bytes(12, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
+    assert L.mq_gemm_workspace_bytes(14, 2048, 18944, 3584, 0) == 0
     # q/o: 224 tiles of 256 x 128, one partial round that a split cannot double
     assert L.mq_gemm_workspace_bytes(0, 2048, 3584, 3584, 0) == 0
     assert L.mq_gemm_workspace_bytes(0, 64, 512, 512, 1) == 0

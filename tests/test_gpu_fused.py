@@ -52,6 +52,22 @@ def test_integer_exact(fmt, M, N, K, split):
     assert np.array_equal(Y.astype(np.float64), Yref)
 
 
+@pytest.mark.parametrize("fmt", [12, 8])
+def test_large_tile_mixed_grid_integer_exact(fmt):
+    """Q4_K and Q8_0 take the 256 x 256 tile once a full round of such tiles
+    exists: M = 2048, N = 8448 gives 264 tiles, one round over all of K plus 8
+    K-split tail tiles.  Integer weights and activations keep every partial sum
+    exact, so sampled rows across both kinds of tile must equal the oracle."""
+    M, N, K = 2048, 8448, 2048
+    q = synth.weights(fmt, synth.rng(34, 0, fmt, 0), N, K, mode="integer")
+    x = synth.activations(synth.rng(34, role=1), M, K, mode="integer")
+    Y = to_host(_fused(fmt, x, q, N, K))
+    rows = np.unique(np.concatenate([[0, 255, 1023, 1024, 2047],
+                                     np.random.default_rng(34).choice(M, 24)]))
+    Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(fmt, q, N, K))
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
+
+
 @pytest.mark.parametrize("fmt,M,N,K", [(12, 64, 512, 512), (12, 129, 200, 1280),
                                        (14, 257, 96, 768), (8, 65, 333, 4128),
                                        (8, 1, 1, 32), (14, 1, 3, 256)])
