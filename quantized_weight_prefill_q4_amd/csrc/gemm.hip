@@ -645,15 +645,21 @@ hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The kernel for the plan's exact (BM, BN); a plan no kernel implements is an
+// error, never a launch with a mismatched tile (its grid would address tiles
+// past the matrix).
 template <int FMT>
 hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t stream) {
-    if constexpr (FMT != kFmtQ6_K)
-        if (bn == 256) return launch_tile<256, 256, FMT>(a, grid, stream);
-    switch (bm) {
-    case 64: return launch_tile<64, 128, FMT>(a, grid, stream);
-    case 128: return launch_tile<128, 128, FMT>(a, grid, stream);
-    default: return launch_tile<256, 128, FMT>(a, grid, stream);
+    if (bm == 256 && bn == 256) {
+        if constexpr (FMT != kFmtQ6_K) return launch_tile<256, 256, FMT>(a, grid, stream);
+    } else if (bm == 256 && bn == 128) {
+        return launch_tile<256, 128, FMT>(a, grid, stream);
+    } else if (bm == 128 && bn == 128) {
+        return launch_tile<128, 128, FMT>(a, grid, stream);
+    } else if (bm == 64 && bn == 128) {
+        return launch_tile<64, 128, FMT>(a, grid, stream);
     }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
