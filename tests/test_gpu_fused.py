@@ -132,3 +132,14 @@ def test_fused_expands_golden_blocks():
         e, v = tok.split(":")
         assert Y[int(e), 0] == float(v), tok
     assert np.float16(Y[0, 1]).view(np.uint16) == 0x3C02
+
+
+def test_large_k_q80_exact():
+    """Fused Q8_0 at K = 32768 (1024 blocks per row, 512 k-steps): integer
+    weights (d = 1, q in -127..127) and activations in -2..2 keep |Y| < 2^24."""
+    M, N, K = 70, 257, 32768
+    q = synth.weights(8, synth.rng(35, 0, 8, 0), N, K, mode="integer")
+    x = synth.activations(synth.rng(35, role=1), M, K, mode="integer")
+    Y = to_host(_fused(8, x, q, N, K))
+    Yref, _ = oracle.gemm_ref(x, oracle.dequant_ref(8, q, N, K))
+    assert np.array_equal(Y.astype(np.float64), Yref)

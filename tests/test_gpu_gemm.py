@@ -148,3 +148,18 @@ def test_7b_shapes_m2048_sampled_rows(name, fmt, N, K):
     rows = np.concatenate([[0, 255, 256, 2047], rows])
     check_gemm(Y[rows], x, w16, K, f"7B {name}", rows=rows)
     assert np.all(np.isfinite(Y))
+
+
+@pytest.mark.parametrize("split", [0, 1])
+def test_large_k_padded_strides_exact(split):
+    """K = 65536 with padded strides (ldx = K + 8, ldw = K + 64): 1024 k-steps
+    in one tile (split 1) or 16 K ranges (auto).  Small-integer operands keep
+    every partial sum below 2^24, so the result is exact and any lost, repeated
+    or misaddressed k-step shows."""
+    M, N, K = 64, 300, 65536
+    g = np.random.default_rng(25)
+    x = g.integers(-2, 3, (M, K)).astype(np.float16).view(np.uint16)
+    w = g.integers(-2, 3, (N, K)).astype(np.float16).view(np.uint16)
+    Y, _ = _gemm(_padded(x, K + 8), _padded(w, K + 64), K, split_k=split)
+    Yref, _ = oracle.gemm_ref(x, w)
+    assert np.array_equal(Y.astype(np.float64), Yref)
