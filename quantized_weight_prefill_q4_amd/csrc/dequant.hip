@@ -67,7 +67,7 @@ __device__ __forceinline__ void decode_q4k(const uint8_t *blk, uint32_t e0, floa
     const float A = f16_bits_to_f32(h.x) * (float)sc;          // exact
     const float C = f16_bits_to_f32(h.x >> 16) * (float)m;     // exact
     const uint32_t n4 = (r >= 32) ? 4 : 0;
-    const uint32_t w0 = (qq.x >> n4) & 0x0F0F0F0Fu, w1 = (qq.y >> n4) & 0x0F0F0F0Fu;
+    const uint32_t w0 = opaque((qq.x >> n4) & 0x0F0F0F0Fu), w1 = opaque((qq.y >> n4) & 0x0F0F0F0Fu);
     // A·q is exact, so one fused rounding equals fl32(A·q − C)
     v[0] = __builtin_fmaf(A, ubyte_f32<0>(w0), -C);
     v[1] = __builtin_fmaf(A, ubyte_f32<1>(w0), -C);
@@ -94,8 +94,8 @@ __device__ __forceinline__ void decode_q6k(const uint8_t *blk, uint32_t e0, floa
     const float d = f16_bits_to_f32(lds_u16(blk + 208));
     const float ds = d * s;  // exact
     const uint32_t n4 = grp >= 2 ? 4 : 0, h2 = 2 * grp;
-    const uint32_t q0 = ((lo0 >> n4) & 0x0F0F0F0Fu) | (((hi0 >> h2) & 0x03030303u) << 4);
-    const uint32_t q1 = ((lo1 >> n4) & 0x0F0F0F0Fu) | (((hi1 >> h2) & 0x03030303u) << 4);
+    const uint32_t q0 = opaque(((lo0 >> n4) & 0x0F0F0F0Fu) | (((hi0 >> h2) & 0x03030303u) << 4));
+    const uint32_t q1 = opaque(((lo1 >> n4) & 0x0F0F0F0Fu) | (((hi1 >> h2) & 0x03030303u) << 4));
     v[0] = ds * (ubyte_f32<0>(q0) - 32.0f);
     v[1] = ds * (ubyte_f32<1>(q0) - 32.0f);
     v[2] = ds * (ubyte_f32<2>(q0) - 32.0f);

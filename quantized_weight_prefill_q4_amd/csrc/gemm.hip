@@ -163,6 +163,8 @@ __device__ __forceinline__ u32x4 pack8(float v0, float v1, float v2, float v3, f
 
 // Q4_K: value fl32(A·q − C), A = d·sc, C = dmin·m, for the 8 nibbles of two dwords.
 __device__ __forceinline__ u32x4 q4k_chunk(uint32_t w0, uint32_t w1, float A, float C) {
+    w0 = opaque(w0);
+    w1 = opaque(w1);
     return pack8(__builtin_fmaf(A, ubyte_f32<0>(w0), -C), __builtin_fmaf(A, ubyte_f32<1>(w0), -C),
                  __builtin_fmaf(A, ubyte_f32<2>(w0), -C), __builtin_fmaf(A, ubyte_f32<3>(w0), -C),
                  __builtin_fmaf(A, ubyte_f32<0>(w1), -C), __builtin_fmaf(A, ubyte_f32<1>(w1), -C),
@@ -232,11 +234,12 @@ struct Q4KLoader {
     }
 };
 
-// 16 bytes at a 2-byte-aligned offset, from the 5 aligned dwords w[0..4].
-__device__ __forceinline__ u32x4 realign16(const uint32_t w[5], bool odd_half) {
-    return odd_half ? u32x4{shift2(w[1], w[0]), shift2(w[2], w[1]), shift2(w[3], w[2]),
-                            shift2(w[4], w[3])}
-                    : u32x4{w[0], w[1], w[2], w[3]};
+// 16 bytes at a 2-byte-aligned offset, from the 5 aligned dwords w[0..4]:
+// sh = 2 when the field starts at the upper half of w[0], else 0 (one
+// v_alignbyte per dword, no select).
+__device__ __forceinline__ u32x4 realign16(const uint32_t w[5], uint32_t sh) {
+    return u32x4{__builtin_amdgcn_alignbyte(w[1], w[0], sh), __builtin_amdgcn_alignbyte(w[2], w[1], sh),
+                 __builtin_amdgcn_alignbyte(w[3], w[2], sh), __builtin_amdgcn_alignbyte(w[4], w[3], sh)};
 }
 
 __device__ __forceinline__ void load5(__amdgpu_buffer_rsrc_t rs, uint32_t o, uint32_t w[5]) {
@@ -251,6 +254,8 @@ __device__ __forceinline__ void load5(__amdgpu_buffer_rsrc_t rs, uint32_t o, uin
 
 // Q6_K: 4 elements (bytes of q) of one dword, value (d·s)·(q − 32).
 __device__ __forceinline__ u32x4 q6k_chunk(uint32_t q0, uint32_t q1, float ds) {
+    q0 = opaque(q0);
+    q1 = opaque(q1);
     return pack8(ds * (ubyte_f32<0>(q0) - 32.0f), ds * (ubyte_f32<1>(q0) - 32.0f),
                  ds * (ubyte_f32<2>(q0) - 32.0f), ds * (ubyte_f32<3>(q0) - 32.0f),
                  ds * (ubyte_f32<0>(q1) - 32.0f), ds * (ubyte_f32<1>(q1) - 32.0f),
@@ -307,13 +312,13 @@ struct Q6KLoader {
         const uint32_t n4 = gp ? 4 : 0, sh_a = 4 * gp, sh_b = 4 * gp + 2;
         const uint32_t L = 0x0F0F0F0Fu, H = 0x03030303u;
         const int r = (i * kThreads + (int)threadIdx.x) >> 1;
-        const bool oh = odd[set][i] != 0;
-        const u32x4 a = realign16(wa[set][i], oh), b = realign16(wb[set][i], oh),
-                    hh = realign16(wh[set][i], oh);
+        const uint32_t sh = odd[set][i];   // 0 or 2
+        const u32x4 a = realign16(wa[set][i], sh), b = realign16(wb[set][i], sh),
+                    hh = realign16(wh[set][i], sh);
         const uint32_t bsa = 8 * osc[set][i], bsb = 8 * ((osc[set][i] + 2) & 3);
         const float sa = (float)(int)(int8_t)((wsa[set][i] >> bsa) & 0xFF);
         const float sbv = (float)(int)(int8_t)((wsb[set][i] >> bsb) & 0xFF);
-        const float d = f16_bits_to_f32(oh ? (wd[set][i] >> 16) : wd[set][i]);
+        const float d = f16_bits_to_f32(__builtin_amdgcn_alignbyte(wd[set][i], wd[set][i], sh));
         const float dsa = d * sa, dsb = d * sbv;
         const uint32_t qa0 = ((a.x >> n4) & L) | (((hh.x >> sh_a) & H) << 4);
         const uint32_t qa1 = ((a.y >> n4) & L) | (((hh.y >> sh_a) & H) << 4);

@@ -34,6 +34,15 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Hide what the optimizer knows about a value's bits.  Applied to a masked
+// dword before its bytes are converted, it keeps each conversion a single
+// v_cvt_f32_ubyteK: knowing the high nibbles are zero, the optimizer would
+// otherwise rewrite "byte k" as a 4-bit field extract plus a conversion.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // Byte k (0..3) of a dword as float (exact); lowers to v_cvt_f32_ubyteK.
 template <int k>
 __device__ __forceinline__ float ubyte_f32(uint32_t w) {
