@@ -603,6 +603,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Args a) {
         cols = a.N - n0;
     }
     const int col_l = lane & 31, row_l = (lane >> 5) * 4;
+    if constexpr (BM == 256) {
+        // Full tile, 16-byte-aligned rows: each 32x32 block goes through a
+        // private 32 x 36-float LDS patch of the wave (the first A stage, idle
+        // after the last step) so that every lane then stores 4 consecutive
+        // columns of one row — a quarter of the store instructions of the
+        // column-per-lane layout.
+        if (rows >= BM && cols >= BN && (ldo & 3) == 0) {
+            constexpr int PS = 36;   // patch row stride in floats (keeps 16-byte rows)
+            float *patch = reinterpret_cast<float *>(A0) + wave * (32 * PS);
+            sync_lds();              // every wave is done reading the stages
+            const int rr = lane >> 3, cc = 4 * (lane & 7);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        patch[((r >> 2) * 8 + row_l + (r & 3)) * PS + col_l] = acc[i][j][r];
+                    // lanes read what other lanes wrote: the LDS runs one wave's
+                    // instructions in order, so only the compiler must keep them
+                    asm volatile("" ::: "memory");
+                    float *dst = out + (int64_t)(wm * TM + i * 32 + rr) * ldo + wn * TN + j * 32 + cc;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<f32x4 *>(dst + (int64_t)(8 * q) * ldo) =
+                            *reinterpret_cast<const f32x4 *>(patch + (rr + 8 * q) * PS + cc);
+                    asm volatile("" ::: "memory");
+                }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
