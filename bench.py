@@ -62,12 +62,18 @@ def parse():
     p.add_argument("--layers", type=int, default=synth.N_LAYERS_7B)
     p.add_argument("--load-reps", type=int, default=3)
     p.add_argument("--fused-steps", type=int, default=5)
+    p.add_argument("--grouped-steps", type=int, default=5,
+                   help="steps of the grouped forward (q|k|v, gate|up as one GEMM each); 0 = skip")
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048,
-                   help="token rows of the oracle sample (one layer's 7 matrices)")
+                   help="token rows of the oracle sample")
+    p.add_argument("--cpu-layers", type=int, default=4,
+                   help="layers (7 matrices each) of the oracle sample")
     p.add_argument("--only-shape", default=None,
                    help="profiling aid: run only this 7B matrix's cache GEMM --steps times")
+    p.add_argument("--only-load", action="store_true",
+                   help="profiling aid: run only the batched decode of the 7B weight set --steps times")
     p.add_argument("--calib-copy", action="store_true",
                    help="profiling aid: run only a plain 1 GiB device copy --steps times "
                         "(the reference for the HBM byte counters)")
@@ -199,7 +205,9 @@ def forward_fused(mq, W, xa, xf, ys, ws):
 
 
 def sweep(torch, mq, dev, log_rows):
-    """Fused vs cache GEMM time per (shape, M); rotates weight copies over > 512 MB."""
+    """Fused vs cache GEMM time per (shape, M); rotates weight copies over > 512 MB.
+    When the crossover falls between two sweep points, the refinement points
+    between them are measured too."""
     out = {}
     for si, (name, fmt, N, K) in enumerate(synth.SWEEP_8B):
         q0 = synth.weights_device(fmt, 5000 + si, N, K, dev)
@@ -210,7 +218,8 @@ def sweep(torch, mq, dev, log_rows):
         qs = [q0] + [q0.clone() for _ in range(nq - 1)]
         x = synth.activations_device(6000 + si, max(synth.SWEEP_M), K, dev)
         res = {}
-        for M in synth.SWEEP_M:
+
+        def measure(M):
             xm = x[:M]
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             ws_c = torch.empty(max(1, mq.workspace_bytes(0, M, N, K) // 4), dtype=torch.float32, device=dev)
@@ -236,24 +245,95 @@ def sweep(torch, mq, dev, log_rows):
                       "fused_tflops": round(flops / t["fused"] / 1e6, 1)}
             log_rows.append(f"  {name:16s} M={M:5d}  cache {t['cache']:9.1f} us ({res[M]['cache_tflops']:7.1f} TF/s)"
                             f"  fused {t['fused']:9.1f} us ({res[M]['fused_tflops']:7.1f} TF/s)")
-        wins = [M for M in synth.SWEEP_M if res[M]["cache_us"] < res[M]["fused_us"]]
-        if not wins:
-            cross = f">{max(synth.SWEEP_M)}"
-        elif wins[0] == min(synth.SWEEP_M):
-            cross = f"<={min(synth.SWEEP_M)}"
-        else:
-            cross = str(wins[0])
-        out[name] = {"crossover_M": cross, "by_M": res}
+
+        def crossover():
+            ms = sorted(res)
+            wins = [M for M in ms if res[M]["cache_us"] < res[M]["fused_us"]]
+            if not wins:
+                return f">{max(ms)}", None
+            if wins[0] == ms[0]:
+                return f"<={ms[0]}", None
+            return str(wins[0]), (ms[ms.index(wins[0]) - 1], wins[0])
+
+        for M in synth.SWEEP_M:
+            measure(M)
+        cross, between = crossover()
+        if between:
+            for M in synth.SWEEP_REFINE:
+                if between[0] < M < between[1]:
+                    measure(M)
+            cross, _ = crossover()
+        out[name] = {"crossover_M": cross, "by_M": {m: res[m] for m in sorted(res)}}
         del caches, qs, cache0, q0
         torch.cuda.empty_cache()
     return out
+
+
+def grouped_forward(torch, mq, W, xa, xf, steps, dev):
+    """The forward with the shared-input GEMMs grouped: per layer one q|k|v GEMM
+    (N = 4608), o, one gate|up GEMM (N = 37888) and down — 112 calls instead of
+    196.  The grouped caches are decoded by one batched call straight into row
+    slices of one buffer per group; the products are the same.  Returns
+    (median ms per step, min ms per step)."""
+    M = xa.shape[0]
+    groups = []
+    jobs = []
+    for row in W:
+        qkv = torch.empty((3584 + 512 + 512, 3584), dtype=torch.float16, device=dev)
+        gu = torch.empty((2 * 18944, 3584), dtype=torch.float16, device=dev)
+        r0 = 0
+        for name in ("q", "k", "v"):
+            fmt, N, K, q, _ = row[name]
+            jobs.append((q, fmt, N, K, qkv[r0:r0 + N]))
+            r0 += N
+        r0 = 0
+        for name in ("gate", "up"):
+            fmt, N, K, q, _ = row[name]
+            jobs.append((q, fmt, N, K, gu[r0:r0 + N]))
+            r0 += N
+        groups.append((qkv, row["o"][4], gu, row["down"][4]))
+    mq.dequant_to_f16_batch(jobs)
+    y_qkv = torch.empty((M, 4608), dtype=torch.float32, device=dev)
+    y_o = torch.empty((M, 3584), dtype=torch.float32, device=dev)
+    y_gu = torch.empty((M, 37888), dtype=torch.float32, device=dev)
+    y_d = torch.empty((M, 3584), dtype=torch.float32, device=dev)
+    wsb = max(mq.workspace_bytes(0, M, N, K) for N, K in ((4608, 3584), (3584, 3584), (37888, 3584), (3584, 18944)))
+    ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
+
+    def step():
+        for qkv, o, gu, down in groups:
+            mq.gemm_f16cache(xa, qkv, 3584, out=y_qkv, ws=ws)
+            mq.gemm_f16cache(xa, o, 3584, out=y_o, ws=ws)
+            mq.gemm_f16cache(xa, gu, 3584, out=y_gu, ws=ws)
+            mq.gemm_f16cache(xf, down, 18944, out=y_d, ws=ws)
+
+    step()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        evs[i].record()
+        step()
+    evs[steps].record()
+    torch.cuda.synchronize()
+    d = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    del groups, jobs
+    return statistics.median(d), min(d)
 
 
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(rows: int):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(rows: int, n_layers: int):
     import oracle
 
     try:
@@ -262,30 +342,47 @@ def cpu_baseline(rows: int):
             if threadpoolctl.threadpool_info() else 1
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    t_deq = t_gemm = 0.0
+    t_deq = t_gemm = t_blas = 0.0
     deq_bytes = 0
-    for mi, (name, fmt, N, K) in enumerate(synth.LAYER_7B):
-        q = synth.weights(fmt, synth.rng(5, 0, mi, 0), N, K)
-        x = synth.activations(synth.rng(5, 0, mi, 1), rows, K)
+    flops = 0.0
+    for li, mi in ((li, mi) for li in range(n_layers) for mi in range(len(synth.LAYER_7B))):
+        name, fmt, N, K = synth.LAYER_7B[mi]
+        q = synth.weights(fmt, synth.rng(5, li, mi, 0), N, K)
+        x = synth.activations(synth.rng(5, li, mi, 1), rows, K)
         t0 = time.perf_counter()
         w16 = oracle.dequant_ref(fmt, q, N, K)
         t1 = time.perf_counter()
         oracle.gemm_ref(x, w16, K)
         t2 = time.perf_counter()
+        # context only: the same product as an f32 BLAS call on the decoded weights
+        xf32 = x.view(np.float16).astype(np.float32)
+        wf32 = w16.view(np.float16).astype(np.float32)
+        t3 = time.perf_counter()
+        xf32 @ wf32.T
+        t4 = time.perf_counter()
         t_deq += t1 - t0
         t_gemm += t2 - t1
+        t_blas += t4 - t3
         deq_bytes += q.nbytes + 2 * N * K
+        flops += 2.0 * rows * N * K
     layers = synth.N_LAYERS_7B
+    t_gemm /= n_layers
+    t_deq /= n_layers
+    t_blas /= n_layers
     return {
         "value": round(rows / (t_gemm * layers), 2),
         "unit": "tok/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"1 of {layers} layers (its 7 matrices), {rows} of 2048 token rows; "
-                   f"f64 oracle gemm_ref (Y and S); tok/s = rows / (layer time x {layers})"),
+        "sample": (f"{n_layers} of {layers} layers (7 matrices each), {rows} of 2048 token rows; "
+                   f"f64 oracle gemm_ref (Y and S); tok/s = rows / (mean layer time x {layers})"),
+        "cpu_model": cpu_model(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
         "gemm_layer_s": round(t_gemm, 3),
-        "dequant_gbs": round(deq_bytes / t_deq / 1e9, 3),
+        "dequant_gbs": round(deq_bytes / (t_deq * n_layers) / 1e9, 3),
         "dequant_layer_s": round(t_deq, 3),
+        "f32_blas_tflops": round(flops / (t_blas * n_layers) / 1e12, 3),
+        "f32_blas_tok_s": round(rows / (t_blas * layers), 2),
     }
 
 
@@ -312,6 +409,17 @@ def main():
         return
     if args.only_shape:
         run_only_shape(torch, mq, args.only_shape, args.steps, dev)
+        return
+    if args.only_load:
+        W = make_weights(torch, mq, args.layers, dev)
+        jobs = [(q, fmt, N, K, cache) for row in W for fmt, N, K, q, cache in row.values()]
+        for _ in range(args.steps):
+            mq.dequant_to_f16_batch(jobs)
+        torch.cuda.synchronize()
+        qb = sum(j[0].numel() for j in jobs)
+        cb = sum(j[2] * j[3] * 2 for j in jobs)
+        print(json.dumps({"only_load": len(jobs), "loads": args.steps, "quant_bytes": qb,
+                          "cache_bytes": cb}), flush=True)
         return
     M, layers = args.M, args.layers
     log(f"[bench] device {torch.cuda.get_device_name(0)}, library {mq.LIB_PATH}")
@@ -361,7 +469,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
-    ev_step_ms = statistics.median(e[0].elapsed_time(e[-1]) for e in steps_events)
+    step_ms = [e[0].elapsed_time(e[-1]) for e in steps_events]
+    ev_step_ms = statistics.median(step_ms)
+    min_step_ms = min(step_ms)
 
     # per-call durations (median over steps), per shape and for the roofline kernel
     per_call = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(calls))]
@@ -387,6 +497,17 @@ def main():
     log(f"[bench] roofline kernel ({ROOFLINE_KERNEL}, {len(dom)} calls/step): "
         f"{ach:.0f} TFLOP/s = {100 * ach / PEAK_F16_TFLOPS:.1f}% of {PEAK_F16_TFLOPS:.0f}, "
         f"avg call {avg_launch_us:.1f} us; traffic {traffic} B/call ({traffic_note})")
+
+    # -- grouped shared-input forward (q|k|v and gate|up as one GEMM each) ------------
+    grouped = None
+    if args.grouped_steps > 0:
+        g_med, g_min = grouped_forward(torch, mq, W, xa, xf, args.grouped_steps, dev)
+        grouped = {"ms_per_step_median": round(g_med, 3), "ms_per_step_min": round(g_min, 3),
+                   "tok_s": round(M / (g_med / 1e3), 1),
+                   "tflops": round(flops.sum() / (g_med / 1e3) / 1e12, 1), "gemms_per_step": 4 * layers}
+        log(f"[bench] grouped forward (4 GEMMs per layer): {g_med:.3f} ms/step median, "
+            f"{grouped['tok_s']:.0f} tok/s, {grouped['tflops']:.0f} TFLOP/s")
+        torch.cuda.empty_cache()
 
     # -- fused forward (no cache) ---------------------------------------------------
     fused = None
@@ -420,7 +541,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         t0 = time.time()
-        cpu = cpu_baseline(args.cpu_rows)
+        cpu = cpu_baseline(args.cpu_rows, args.cpu_layers)
         log(f"[bench] cpu oracle: {cpu['value']} tok/s on {cpu['cores']} threads "
             f"({time.time() - t0:.1f}s)")
 
@@ -432,6 +553,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median_events": round(ev_step_ms, 4),
+        "ms_per_step_min_events": round(min_step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -461,6 +584,7 @@ def main():
             "frac": round(deq_gbs / PEAK_HBM_GBS, 4),
         },
         "fused": fused,
+        "grouped_forward": grouped,
         "crossover": cross,
         "cpu_baseline": cpu,
     }

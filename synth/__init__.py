@@ -120,6 +120,8 @@ SWEEP_8B = (
     ("q80_4096x4096", Q8_0, 4096, 4096),
 )
 SWEEP_M = (128, 512, 1024, 2048)
+# extra M points measured when the crossover falls between two sweep points
+SWEEP_REFINE = (256, 384, 768)
 
 
 # ---------------------------------------------------------------------------

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import (announce, check_gemm, f16_bits, needs_gpu, to_dev_f16, to_dev_u8,
+from gpu_common import (announce, check_gemm, dev, f16_bits, needs_gpu, to_dev_f16, to_dev_u8,
                         to_host)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -163,3 +163,34 @@ def test_large_k_padded_strides_exact(split):
     Y, _ = _gemm(_padded(x, K + 8), _padded(w, K + 64), K, split_k=split)
     Yref, _ = oracle.gemm_ref(x, w)
     assert np.array_equal(Y.astype(np.float64), Yref)
+
+
+def test_grouped_shared_input_gemm_exact():
+    """Shared-input weights grouped into one cache (q|k|v-like: 300 + 64 + 64 rows),
+    each decoded by one batched call into its row slice, then one GEMM: Y of the
+    group equals the separate GEMMs column block by column block, and the oracle,
+    exactly (integer mode)."""
+    K, M = 1024, 130
+    parts = [(12, 300), (12, 64), (14, 64)]
+    qs = [synth.weights(f, synth.rng(26, 0, i, 0), n, K, mode="integer") for i, (f, n) in enumerate(parts)]
+    rows = sum(n for _, n in parts)
+    dev_q = [to_dev_u8(q) for q in qs]
+    group = torch.empty((rows, mq.cache_ld(K)), dtype=torch.float16, device=dev())
+    jobs, r0 = [], 0
+    for (f, n), dq in zip(parts, dev_q):
+        jobs.append((dq, f, n, K, group[r0:r0 + n]))
+        r0 += n
+    announce("dequant_batch", "group of 3 into row slices")
+    mq.dequant_to_f16_batch(jobs)
+    x = synth.activations(synth.rng(26, role=1), M, K, mode="integer")
+    announce("gemm_f16cache", "grouped", f"M={M} N={rows} K={K}")
+    Yg = to_host(mq.gemm_f16cache(to_dev_f16(x), group, K))
+    w16 = np.concatenate([oracle.dequant_ref(f, q, n, K) for (f, n), q in zip(parts, qs)])
+    Yref, _ = oracle.gemm_ref(x, w16)
+    assert np.array_equal(Yg.astype(np.float64), Yref)
+    r0 = 0
+    for (f, n), dq in zip(parts, dev_q):
+        c = mq.dequant_to_f16(dq, f, n, K)
+        Ys = to_host(mq.gemm_f16cache(to_dev_f16(x), c, K))
+        assert np.array_equal(Ys, Yg[:, r0:r0 + n])
+        r0 += n
