@@ -8,8 +8,8 @@ it; the product path never calls it.
 
 What it computes (sources are the four pages the method is described on):
 
-* ``dequant_ref`` — decode of GGUF Q4_K / Q6_K / Q8_0 blocks into f16 bit
-  patterns.  minfer "05 · 8p — Persistent f16 weight cache + fused
+* ``dequant_ref`` — decode of GGUF Q4_K / Q6_K / Q8_0 (and Q4_0 / Q5_0 / Q5_1
+  / Q5_K) blocks into f16 bit patterns.  minfer "05 · 8p — Persistent f16 weight cache + fused
   dequant-in-GEMM", §2 Principle and §3.2 (third site): weights are decoded in
   f32 and rounded once to f16 per element, the same path for the standalone
   dequant and for the fused kernel.
@@ -29,7 +29,11 @@ from .f16 import f16_bits_to_float, f32_to_f16_bits, f64_to_f32
 from .formats import (
     BLOCK_BYTES,
     BLOCK_ELEMS,
+    Q4_0,
     Q4_K,
+    Q5_0,
+    Q5_1,
+    Q5_K,
     Q6_K,
     Q8_0,
     cache_ld,
@@ -44,7 +48,11 @@ from .gemm import gemm_ref, gemm_bruteforce, within_tolerance
 __all__ = [
     "BLOCK_BYTES",
     "BLOCK_ELEMS",
+    "Q4_0",
     "Q4_K",
+    "Q5_0",
+    "Q5_1",
+    "Q5_K",
     "Q6_K",
     "Q8_0",
     "cache_ld",

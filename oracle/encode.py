@@ -1,4 +1,4 @@
-"""Field-wise encoders of the three block formats (inverse of the decoders).
+"""Field-wise encoders of the block formats (inverse of the decoders).
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
@@ -60,6 +60,53 @@ def pack_q80(d_bits: int, q) -> bytes:
     q = [int(v) for v in q]
     assert len(q) == 32 and all(-128 <= v < 128 for v in q)
     return bytes([d_bits & 255, d_bits >> 8] + [v & 255 for v in q])
+
+
+def _nibble_bytes32(q) -> list[int]:
+    """16 bytes holding 32 four-bit values: element j < 16 in the low nibble of
+    byte j, element j + 16 in its high nibble."""
+    return [(q[j] & 15) | ((q[j + 16] & 15) << 4) for j in range(16)]
+
+
+def _u32_le(v: int) -> list[int]:
+    return [(v >> (8 * i)) & 255 for i in range(4)]
+
+
+def pack_q40(d_bits: int, q) -> bytes:
+    """One Q4_0 block from f16 bits of d and 32 four-bit quants (0..15)."""
+    q = [int(v) for v in q]
+    assert len(q) == 32 and all(0 <= v < 16 for v in q)
+    return bytes([d_bits & 255, d_bits >> 8] + _nibble_bytes32(q))
+
+
+def pack_q50(d_bits: int, q) -> bytes:
+    """One Q5_0 block from f16 bits of d and 32 five-bit quants (0..31)."""
+    q = [int(v) for v in q]
+    assert len(q) == 32 and all(0 <= v < 32 for v in q)
+    qh = sum(((v >> 4) & 1) << j for j, v in enumerate(q))
+    return bytes([d_bits & 255, d_bits >> 8] + _u32_le(qh) + _nibble_bytes32(q))
+
+
+def pack_q51(d_bits: int, m_bits: int, q) -> bytes:
+    """One Q5_1 block from f16 bits of d and m and 32 five-bit quants (0..31)."""
+    q = [int(v) for v in q]
+    assert len(q) == 32 and all(0 <= v < 32 for v in q)
+    qh = sum(((v >> 4) & 1) << j for j, v in enumerate(q))
+    return bytes([d_bits & 255, d_bits >> 8, m_bits & 255, m_bits >> 8] + _u32_le(qh)
+                 + _nibble_bytes32(q))
+
+
+def pack_q5k(d_bits: int, dmin_bits: int, sc, mn, q) -> bytes:
+    """One Q5_K block from f16 bits of d and dmin, 8 six-bit scales, 8 six-bit
+    mins and 256 five-bit quants (0..31) in element order."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 32 for v in q)
+    # the scale bytes, the low nibbles and the layout of d / dmin are Q4_K's
+    q4 = pack_q4k(d_bits, dmin_bits, sc, mn, [v & 15 for v in q])
+    qh = [0] * 32
+    for e in range(256):
+        qh[e % 32] |= ((q[e] >> 4) & 1) << (e // 32)
+    return bytes(q4[:16]) + bytes(qh) + bytes(q4[16:144])
 
 
 def concat_blocks(blocks) -> np.ndarray:

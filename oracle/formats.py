@@ -26,6 +26,23 @@ Rounding (the pages: float math, then one conversion to half):
   rounding is to f16.  IEEE signed zeros are kept: s = 0 with q < 32 gives −0.
 * Q8_0: d·q, exact in f32, one rounding to f16.
 
+Four more formats of the same family (the pages' coverage list: minfer "79 ·
+Phase-8 coverage & first-measurement batch" §3.4 and §3.6, and "05 · 8p"
+§2–§3.2 for Q5_0):
+* Q4_0 (18 B): f16 d, 16 bytes of nibbles; element j < 16 is the low nibble
+  of byte j, element j + 16 its high nibble; value d·(q − 8).  Exact in f32.
+* Q5_0 (22 B, page "05 · 8p" §2 / §3.2): f16 d, a 32-bit qh plane, 16 bytes
+  of nibbles; the nibble as Q4_0, plus bit j (element j) of qh as its 16s
+  bit; value d·(q − 16).  Exact in f32.
+* Q5_1 (24 B; qh at byte 4, "05 · 8p" §2): f16 d, f16 m, qh, nibbles as Q5_0;
+  value d·q + m: the product is exact, the sum is the one f32 rounding.
+* Q5_K (176 B, "79" §3.4: transposed qh, deinterleaved qs chunks): f16 d, f16
+  dmin, the 12 scale/min bytes of Q4_K, 32 bytes of qh, 128 bytes of nibbles
+  laid out as Q4_K's; element l of sub-block s takes bit s of qh[l] as its
+  16s bit; value fl32(d·sc·q − dmin·m) as for Q4_K (A·q still exact).
+The pages give no bit positions for Q4_0, Q5_1 and Q5_K; the ones used are
+the GGUF ones, consistent with the pages' Q5_0 layout and Q5_K description.
+
 Two independent decoders live here: ``dequant_scalar`` walks one element at a
 time in Python floats with the hand-written converters of ``oracle.f16``;
 ``dequant_ref`` is a vectorized numpy decode in float32 with numpy's f16 cast.
@@ -40,12 +57,16 @@ from .f16 import f16_bits_to_float, f32_to_f16_bits, f64_to_f32
 
 # GGUF type numbers; minfer's type_id 6 for Q5_0 (page "79 · Phase-8 coverage
 # batch", §3.6) follows the same numbering.
+Q4_0 = 2
+Q5_0 = 6
+Q5_1 = 7
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
 
-BLOCK_ELEMS = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+BLOCK_ELEMS = {Q4_0: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 
 def row_bytes(fmt: int, K: int) -> int:
@@ -126,7 +147,64 @@ def _q80_block_scalar(b) -> list[int]:
     return [f32_to_f16_bits(f64_to_f32(d * float(_i8(b[2 + j])))) for j in range(32)]
 
 
-_SCALAR = {Q4_K: _q4k_block_scalar, Q6_K: _q6k_block_scalar, Q8_0: _q80_block_scalar}
+def _u32(b, off: int) -> int:
+    return _u16(b, off) | (_u16(b, off + 2) << 16)
+
+
+def _nibble32(b, qs_off: int, j: int) -> int:
+    """4-bit quant of element j (0..31) of a 32-element block: low nibble of
+    byte j for j < 16, high nibble of byte j - 16 otherwise."""
+    byte = b[qs_off + (j % 16)]
+    return byte & 15 if j < 16 else byte >> 4
+
+
+def _q40_block_scalar(b) -> list[int]:
+    d = f16_bits_to_float(_u16(b, 0))
+    return [f32_to_f16_bits(f64_to_f32(d * float(_nibble32(b, 2, j) - 8))) for j in range(32)]
+
+
+def _q50_block_scalar(b) -> list[int]:
+    d = f16_bits_to_float(_u16(b, 0))
+    qh = _u32(b, 2)
+    out = []
+    for j in range(32):
+        q = _nibble32(b, 6, j) + 16 * ((qh >> j) & 1)
+        out.append(f32_to_f16_bits(f64_to_f32(d * float(q - 16))))
+    return out
+
+
+def _q51_block_scalar(b) -> list[int]:
+    d = f16_bits_to_float(_u16(b, 0))
+    m = f16_bits_to_float(_u16(b, 2))
+    qh = _u32(b, 4)
+    out = []
+    for j in range(32):
+        q = _nibble32(b, 8, j) + 16 * ((qh >> j) & 1)
+        # d*q is exact; d*q + m is exact in binary64 and rounds once to f32
+        out.append(f32_to_f16_bits(f64_to_f32(d * q + m)))
+    return out
+
+
+def _q5k_block_scalar(b) -> list[int]:
+    d = f16_bits_to_float(_u16(b, 0))
+    dmin = f16_bits_to_float(_u16(b, 2))
+    s = [b[4 + i] for i in range(12)]
+    out = []
+    for e in range(256):
+        j = e // 32
+        sc, m = q4k_scale_min(j, s)
+        c, r = divmod(e, 64)
+        l = r % 32
+        byte = b[48 + 32 * c + l]
+        low4 = byte & 15 if r < 32 else byte >> 4
+        q = low4 + 16 * ((b[16 + l] >> j) & 1)
+        out.append(f32_to_f16_bits(f64_to_f32(d * sc * q - dmin * m)))
+    return out
+
+
+_SCALAR = {Q4_K: _q4k_block_scalar, Q6_K: _q6k_block_scalar, Q8_0: _q80_block_scalar,
+           Q4_0: _q40_block_scalar, Q5_0: _q50_block_scalar, Q5_1: _q51_block_scalar,
+           Q5_K: _q5k_block_scalar}
 
 
 def dequant_scalar(fmt: int, qbytes, N: int, K: int) -> np.ndarray:
@@ -201,7 +279,68 @@ def _q80_vec(blk: np.ndarray) -> np.ndarray:
     return V.astype(np.float16).view(np.uint16).reshape(N, nb * 32)
 
 
-_VEC = {Q4_K: _q4k_vec, Q6_K: _q6k_vec, Q8_0: _q80_vec}
+def _nibbles32(qs: np.ndarray) -> np.ndarray:
+    """[..., 16] bytes -> [..., 32] quants: elements 0..15 low nibbles, 16..31 high."""
+    return np.concatenate([qs & 15, qs >> 4], axis=-1)
+
+
+def _qh_bits32(blk: np.ndarray, off: int) -> np.ndarray:
+    """Bit j of the little-endian u32 at byte ``off``, for j = 0..31."""
+    b = blk[..., off:off + 4]
+    bits = np.unpackbits(b, axis=-1, bitorder="little")      # byte 0 bits 0..7, byte 1 ...
+    return bits
+
+
+def _q40_vec(blk: np.ndarray) -> np.ndarray:
+    N, nb, _ = blk.shape
+    d = _f16_field(blk, 0)
+    q = _nibbles32(blk[..., 2:18]).astype(np.float32) - 8.0
+    V = d[..., None] * q
+    return V.astype(np.float16).view(np.uint16).reshape(N, nb * 32)
+
+
+def _q50_vec(blk: np.ndarray) -> np.ndarray:
+    N, nb, _ = blk.shape
+    d = _f16_field(blk, 0)
+    q = _nibbles32(blk[..., 6:22]).astype(np.int32) + 16 * _qh_bits32(blk, 2).astype(np.int32)
+    V = d[..., None] * (q - 16).astype(np.float32)
+    return V.astype(np.float16).view(np.uint16).reshape(N, nb * 32)
+
+
+def _q51_vec(blk: np.ndarray) -> np.ndarray:
+    N, nb, _ = blk.shape
+    d = _f16_field(blk, 0)
+    m = _f16_field(blk, 2)
+    q = _nibbles32(blk[..., 8:24]).astype(np.int32) + 16 * _qh_bits32(blk, 4).astype(np.int32)
+    P = d[..., None] * q.astype(np.float32)          # exact
+    V = P + m[..., None]                             # the one f32 rounding
+    return V.astype(np.float16).view(np.uint16).reshape(N, nb * 32)
+
+
+def _q5k_vec(blk: np.ndarray) -> np.ndarray:
+    N, nb, _ = blk.shape
+    d = _f16_field(blk, 0)
+    dmin = _f16_field(blk, 2)
+    s = blk[..., 4:16].astype(np.int32)
+    sc = np.empty((N, nb, 8), np.int32)
+    mn = np.empty((N, nb, 8), np.int32)
+    sc[..., :4] = s[..., 0:4] & 63
+    mn[..., :4] = s[..., 4:8] & 63
+    sc[..., 4:] = (s[..., 8:12] & 15) | ((s[..., 0:4] >> 6) << 4)
+    mn[..., 4:] = (s[..., 8:12] >> 4) | ((s[..., 4:8] >> 6) << 4)
+    qh = blk[..., 16:48]                                              # [N, nb, 32] byte l
+    hi = np.stack([(qh >> j) & 1 for j in range(8)], axis=2)          # [N, nb, 8, 32]
+    qs = blk[..., 48:176].reshape(N, nb, 4, 32)
+    low = np.stack([qs & 15, qs >> 4], axis=3).reshape(N, nb, 8, 32)
+    q = (low.astype(np.int32) + 16 * hi.astype(np.int32)).astype(np.float32)
+    A = d[..., None] * sc.astype(np.float32)
+    C = dmin[..., None] * mn.astype(np.float32)
+    V = A[..., None] * q - C[..., None]
+    return V.astype(np.float16).view(np.uint16).reshape(N, nb * 256)
+
+
+_VEC = {Q4_K: _q4k_vec, Q6_K: _q6k_vec, Q8_0: _q80_vec, Q4_0: _q40_vec, Q5_0: _q50_vec,
+        Q5_1: _q51_vec, Q5_K: _q5k_vec}
 
 
 def dequant_ref(fmt: int, qbytes: np.ndarray, N: int, K: int) -> np.ndarray:

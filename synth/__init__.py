@@ -13,9 +13,13 @@ Distributions (per matrix, drawn in this order, arrays shaped [N, nb, ...]):
 * Q6_K: 128 uniform bytes of low nibbles; 64 uniform bytes of 2-bit pairs
   (so q is uniform 0..63); 16 int8 scales uniform −32..31; d = f16(|N|·2⁻⁹).
 * Q8_0: d = f16(|N(0,1)|·2⁻⁷); 32 int8 uniform −127..127.
+* Q4_0: d = f16(|N(0,1)|·2⁻⁷); 16 uniform bytes of nibbles.
+* Q5_0: d = f16(|N(0,1)|·2⁻⁷); 4 uniform bytes of qh; 16 uniform bytes.
+* Q5_1: d = f16(|N(0,1)|·2⁻⁷); m = f16(−|N(0,1)|·2⁻³); 4 + 16 uniform bytes.
+* Q5_K: as Q4_K, with 32 uniform bytes of qh between the scales and quants.
 * X: f16(N(0,1)), [M, K].
 
-``mode="integer"`` sets every f16 scale field to 1.0 (d = dmin = 1), so that
+``mode="integer"`` sets every f16 scale field to 1.0 (d = dmin = m = 1), so that
 decoded weights are small integers; with integer X every partial sum of the
 matmul is an exact integer in f32 whatever the summation order.
 """
@@ -27,11 +31,15 @@ import numpy as np
 SEED_BASE = 20260831
 
 # format ids (GGUF type numbers)
+Q4_0 = 2
+Q5_0 = 6
+Q5_1 = 7
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
-_ELEMS = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
-_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+_ELEMS = {Q4_0: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+_BYTES = {Q4_0: 18, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 _ONE_F16 = 0x3C00
 
 
@@ -80,6 +88,30 @@ def weights(fmt: int, g: np.random.Generator, N: int, K: int, mode: str = "rando
             d[:] = _ONE_F16
         _put_u16(blk, 0, d)
         blk[..., 2:34] = g.integers(-127, 128, (N, nb, 32), dtype=np.int8).view(np.uint8)
+    elif fmt in (Q4_0, Q5_0):
+        d = _f16_abs_normal(g, (N, nb), 2.0 ** -7)
+        if mode == "integer":
+            d[:] = _ONE_F16
+        _put_u16(blk, 0, d)
+        blk[..., 2:] = g.integers(0, 256, (N, nb, _BYTES[fmt] - 2), dtype=np.uint8)
+    elif fmt == Q5_1:
+        d = _f16_abs_normal(g, (N, nb), 2.0 ** -7)
+        m = _f16_abs_normal(g, (N, nb), 2.0 ** -3) | np.uint16(0x8000)
+        if mode == "integer":
+            d[:] = _ONE_F16
+            m[:] = _ONE_F16
+        _put_u16(blk, 0, d)
+        _put_u16(blk, 2, m)
+        blk[..., 4:24] = g.integers(0, 256, (N, nb, 20), dtype=np.uint8)
+    elif fmt == Q5_K:
+        d = _f16_abs_normal(g, (N, nb), 2.0 ** -7)
+        dmin = _f16_abs_normal(g, (N, nb), 2.0 ** -7)
+        if mode == "integer":
+            d[:] = _ONE_F16
+            dmin[:] = _ONE_F16
+        _put_u16(blk, 0, d)
+        _put_u16(blk, 2, dmin)
+        blk[..., 4:176] = g.integers(0, 256, (N, nb, 172), dtype=np.uint8)
     else:
         raise ValueError(f"unknown format {fmt}")
     return blk.reshape(N, nb * _BYTES[fmt])
@@ -159,6 +191,19 @@ def weights_device(fmt: int, seed: int, N: int, K: int, device, mode: str = "ran
         q = torch.randint(-127, 128, (N, nb, 32), generator=g, device=device, dtype=torch.int8)
         blk[..., 2:34] = q.view(torch.uint8)
         blk[..., 0:2] = one if mode == "integer" else f16_abs_normal(2.0 ** -7)
+    elif fmt in (Q4_0, Q5_0):
+        blk[..., 0:2] = one if mode == "integer" else f16_abs_normal(2.0 ** -7)
+    elif fmt == Q5_1:
+        blk[..., 0:2] = one if mode == "integer" else f16_abs_normal(2.0 ** -7)
+        if mode == "integer":
+            blk[..., 2:4] = one
+        else:
+            m = f16_abs_normal(2.0 ** -3).clone()
+            m[..., 1] |= 0x80                       # sign bit of the f16 min
+            blk[..., 2:4] = m
+    elif fmt == Q5_K:
+        blk[..., 0:2] = one if mode == "integer" else f16_abs_normal(2.0 ** -7)
+        blk[..., 2:4] = one if mode == "integer" else f16_abs_normal(2.0 ** -7)
     else:
         raise ValueError(f"unknown format {fmt}")
     return blk.view(N, nb * _BYTES[fmt])
