@@ -49,14 +49,30 @@ extern "C" {
  *            w = d·sc·q − dmin·m per 32-element sub-block
  *   MQ_Q6_K: 256 elements in 210 bytes = 128 B low 4 bits, 64 B high 2 bits
  *            of 6-bit q, 16 × int8 scales, f16 d;  w = d·s·(q − 32)
+ * Four more of the family (minfer 79 · Phase-8 coverage batch, §3.4 and §3.6;
+ * minfer 05 · 8p §2 for the Q5_0 layout).  In the 32-element formats element
+ * j < 16 is the low nibble of quant byte j and element j + 16 its high nibble;
+ * the 5-bit formats add bit j of the 32-bit qh plane as the 16s bit:
+ *   MQ_Q4_0: 32 elements in 18 bytes  = f16 d, 16 B q;           w = d·(q − 8)
+ *   MQ_Q5_0: 32 elements in 22 bytes  = f16 d, 4 B qh, 16 B q;   w = d·(q − 16)
+ *   MQ_Q5_1: 32 elements in 24 bytes  = f16 d, f16 m, 4 B qh, 16 B q;
+ *            w = d·q + m
+ *   MQ_Q5_K: 256 elements in 176 bytes = Q4_K's d, dmin and 12 scale/min
+ *            bytes, 32 B qh, 128 B low 4 bits laid out as Q4_K's; element l
+ *            of 32-element sub-block s takes bit s of qh[l] as its 16s bit;
+ *            w = d·sc·q − dmin·m as Q4_K
  * A quantized weight of N rows is N rows of K/block_elems blocks each, rows
- * contiguous (row bytes = K/block_elems · block_bytes).  Q8_0 and Q6_K blocks
- * are only 2-byte aligned inside a row (minfer 05 · 8p §2: alignment of a
- * strided block is stride·g + offset); the library never issues a load that
- * needs more. */
+ * contiguous (row bytes = K/block_elems · block_bytes).  Q8_0, Q6_K, Q4_0 and
+ * Q5_0 blocks are only 2-byte aligned inside a row (minfer 05 · 8p §2:
+ * alignment of a strided block is stride·g + offset); the library never
+ * issues a load that needs more. */
 enum {
+    MQ_Q4_0 = 2,
+    MQ_Q5_0 = 6,
+    MQ_Q5_1 = 7,
     MQ_Q8_0 = 8,
     MQ_Q4_K = 12,
+    MQ_Q5_K = 13,
     MQ_Q6_K = 14
 };
 
@@ -78,10 +94,10 @@ enum {
 #define MQ_MAX_K (1 << 21)       /* K and every leading dimension */
 #define MQ_MAX_SPLIT_K 16
 
-/* Elements per block of `fmt` (32, 256, 256), or MQ_ERR_FORMAT. */
+/* Elements per block of `fmt` (32 or 256), or MQ_ERR_FORMAT. */
 int mq_block_elems(int fmt);
 
-/* Bytes per block of `fmt` (34, 144, 210), or MQ_ERR_FORMAT. */
+/* Bytes per block of `fmt` (18, 22, 24, 34, 144, 176, 210), or MQ_ERR_FORMAT. */
 int mq_block_bytes(int fmt);
 
 /* Bytes of one quantized row of K elements, or a negative MQ_ERR_* code when
@@ -100,9 +116,11 @@ int64_t mq_f16cache_ld(int64_t K);
  *         w16[n·ld + k] = f16 of weight (n, k) for k < K, +0 for K <= k < ld.
  *   ld  : >= K, multiple of 8 (mq_f16cache_ld(K) is the padded choice).
  * Each element is computed in f32 and rounded once to f16 (round to nearest
- * even, subnormals kept, IEEE signed zeros kept): Q4_K as fl32(d·sc·q − dmin·m),
- * Q6_K as (d·s)·(q − 32), Q8_0 as d·q (minfer 05 · 8p §3.2: float math, then
- * one conversion to half).  The result is bit-identical to that definition.
+ * even, subnormals kept, IEEE signed zeros kept): Q4_K and Q5_K as
+ * fl32(d·sc·q − dmin·m), Q6_K as (d·s)·(q − 32), Q8_0 as d·q, Q4_0 as
+ * d·(q − 8), Q5_0 as d·(q − 16), Q5_1 as fl32(d·q + m) (minfer 05 · 8p §3.2:
+ * float math, then one conversion to half).  The result is bit-identical to
+ * that definition.
  * One kernel, one pass over the quantized bytes; HBM-bound. */
 int mq_dequant_to_f16(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld,
                       void *stream);
@@ -110,7 +128,7 @@ int mq_dequant_to_f16(int fmt, const void *wq, int N, int K, uint16_t *w16, int 
 /* One weight of a batched decode (see mq_dequant_to_f16_batch); the fields
  * mean what the same-named arguments of mq_dequant_to_f16 mean. */
 typedef struct mq_dequant_job {
-    int fmt;             /* MQ_Q4_K, MQ_Q6_K or MQ_Q8_0 */
+    int fmt;             /* one of the MQ_Q* formats */
     int N, K;            /* rows; columns, a multiple of the format's block */
     int ld;              /* cache row stride in halves: >= K, multiple of 8 */
     const void *wq;      /* device, 16-byte aligned, N·mq_row_bytes(fmt, K) bytes */
@@ -158,7 +176,7 @@ int mq_gemm_f16cache(const uint16_t *X, int ldx, const uint16_t *W16, int ldw, f
                      void *stream);
 
 /* Y[M×N] = X[M×K] · dequant(Wq)ᵀ with the weight expanded inside the kernel.
- *   fmt : MQ_Q4_K, MQ_Q6_K or MQ_Q8_0; K a multiple of its block.
+ *   fmt : one of the MQ_Q* formats; K a multiple of its block.
  *   wq  : device, 16-byte aligned, N·mq_row_bytes(fmt, K) bytes.
  *   other arguments as mq_gemm_f16cache (ws sized with fmt).
  * The expanded f16 values are bit-identical to mq_dequant_to_f16's (minfer

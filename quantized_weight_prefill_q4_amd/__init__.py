@@ -1,5 +1,6 @@
-"""Prefill matmul over GGUF block-quantized weights (Q4_K, Q6_K, Q8_0) for AMD
-MI355X: a load-time f16 cache with an MFMA GEMM, and a fused dequant-in-GEMM.
+"""Prefill matmul over GGUF block-quantized weights (Q4_K, Q6_K, Q8_0, Q4_0,
+Q5_0, Q5_1, Q5_K) for AMD MI355X: a load-time f16 cache with an MFMA GEMM, and
+a fused dequant-in-GEMM.
 
 The computation lives in the HIP library ``libmq.so`` (C ABI in
 ``include/mq.h``); this package only marshals torch tensors into it.
@@ -7,7 +8,11 @@ The computation lives in the HIP library ``libmq.so`` (C ABI in
 
 from ._lib import (
     LIB_PATH,
+    MQ_Q4_0,
     MQ_Q4_K,
+    MQ_Q5_0,
+    MQ_Q5_1,
+    MQ_Q5_K,
     MQ_Q6_K,
     MQ_Q8_0,
     MQError,
@@ -29,7 +34,11 @@ from .api import (
 __all__ = [
     "FORMATS",
     "LIB_PATH",
+    "MQ_Q4_0",
     "MQ_Q4_K",
+    "MQ_Q5_0",
+    "MQ_Q5_1",
+    "MQ_Q5_K",
     "MQ_Q6_K",
     "MQ_Q8_0",
     "MQError",

@@ -20,8 +20,12 @@ MQ_ERR_WORKSPACE = -6
 MQ_ERR_SPLIT = -7
 MQ_ERR_HIP = -8
 
+MQ_Q4_0 = 2
+MQ_Q5_0 = 6
+MQ_Q5_1 = 7
 MQ_Q8_0 = 8
 MQ_Q4_K = 12
+MQ_Q5_K = 13
 MQ_Q6_K = 14
 
 _c_int, _c_i64, _c_size, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p

@@ -12,9 +12,11 @@ import torch
 
 import ctypes
 
-from ._lib import MQ_Q4_K, MQ_Q6_K, MQ_Q8_0, MqDequantJob, check, lib
+from ._lib import (MQ_Q4_0, MQ_Q4_K, MQ_Q5_0, MQ_Q5_1, MQ_Q5_K, MQ_Q6_K, MQ_Q8_0,
+                   MqDequantJob, check, lib)
 
-FORMATS = {"q8_0": MQ_Q8_0, "q4_k": MQ_Q4_K, "q6_k": MQ_Q6_K}
+FORMATS = {"q4_0": MQ_Q4_0, "q5_0": MQ_Q5_0, "q5_1": MQ_Q5_1, "q8_0": MQ_Q8_0,
+           "q4_k": MQ_Q4_K, "q5_k": MQ_Q5_K, "q6_k": MQ_Q6_K}
 
 
 def _fmt(fmt) -> int:

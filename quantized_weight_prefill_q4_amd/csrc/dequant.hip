@@ -10,10 +10,13 @@
 // workgroup stages the contiguous bytes of its blocks in LDS with one 16-byte
 // load per 16 input bytes, then every thread decodes four 16-byte runs of
 // f16 output, each wave store writing 1 KiB of contiguous cache row.  Q6_K
-// (210 B) and Q8_0 (34 B) blocks are only 2-byte aligned; they are read from
-// LDS with 2-byte accesses, and global memory is only read in aligned
-// 16-byte chunks.  The pad columns [K, ld) are written as +0 by the tail of
-// the grid.
+// (210 B), Q8_0 (34 B), Q4_0 (18 B) and Q5_0 (22 B) blocks are only 2-byte
+// aligned (the Q5_0 qh word in particular: minfer "05 · 8p" §2); they are
+// read from LDS with 2-byte accesses, and global memory is only read in
+// aligned 16-byte chunks.  The pad columns [K, ld) are written as +0 by the
+// tail of the grid.  Formats: Q4_K, Q5_K, Q6_K (256-element super-blocks),
+// Q4_0, Q5_0, Q5_1, Q8_0 (32-element blocks); decode formulas as in the
+// per-format functions below.
 
 #include "mq_device.h"
 #include "mq_internal.h"
@@ -29,6 +32,10 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<kFmtQ4_K> { static constexpr uint32_t BE = 256, BB = 144; };
 template <> struct Fmt<kFmtQ6_K> { static constexpr uint32_t BE = 256, BB = 210; };
 template <> struct Fmt<kFmtQ8_0> { static constexpr uint32_t BE = 32, BB = 34; };
+template <> struct Fmt<kFmtQ4_0> { static constexpr uint32_t BE = 32, BB = 18; };
+template <> struct Fmt<kFmtQ5_0> { static constexpr uint32_t BE = 32, BB = 22; };
+template <> struct Fmt<kFmtQ5_1> { static constexpr uint32_t BE = 32, BB = 24; };
+template <> struct Fmt<kFmtQ5_K> { static constexpr uint32_t BE = 256, BB = 176; };
 
 // blocks per workgroup and their staged bytes (plus up to 16 bytes of lead-in)
 template <int FMT> constexpr uint32_t group_blocks() { return kChunksPerGroup * 8 / Fmt<FMT>::BE; }
@@ -120,6 +127,104 @@ __device__ __forceinline__ void decode_q80(const uint8_t *blk, uint32_t e0, floa
     v[7] = d * sbyte_f32<3>(q1);
 }
 
+// The 16s bits of 4 consecutive elements, bits 0..3 of b, moved to bit 4 of
+// bytes 0..3 (b·(1 + 2^7 + 2^14 + 2^21) puts bit i at bit 8i; no partial
+// products overlap).
+__device__ __forceinline__ uint32_t spread4_to_bit4(uint32_t b) {
+    return ((b * 0x00204081u) & 0x01010101u) << 4;
+}
+
+// 8 four-bit quants of a 32-element block (Q4_0 / Q5_0 / Q5_1 nibble plane at
+// `qs`): elements e0..e0+7 are bytes (e0 & 15) .. +7, low nibbles for e0 < 16.
+__device__ __forceinline__ void nibbles8(const uint8_t *qs, uint32_t e0, uint32_t &w0, uint32_t &w1) {
+    const uint8_t *p = qs + (e0 & 15);
+    const uint32_t n4 = e0 >= 16 ? 4 : 0;
+    w0 = (lds_u32_a2(p) >> n4) & 0x0F0F0F0Fu;
+    w1 = (lds_u32_a2(p + 4) >> n4) & 0x0F0F0F0Fu;
+}
+
+// Q4_0, 8 outputs of the block at `blk` (2-byte aligned): value d·(q − 8).
+__device__ __forceinline__ void decode_q40(const uint8_t *blk, uint32_t e0, float v[8]) {
+    const float d = f16_bits_to_f32(lds_u16(blk));
+    uint32_t w0, w1;
+    nibbles8(blk + 2, e0, w0, w1);
+    w0 = opaque(w0);
+    w1 = opaque(w1);
+    v[0] = d * (ubyte_f32<0>(w0) - 8.0f);
+    v[1] = d * (ubyte_f32<1>(w0) - 8.0f);
+    v[2] = d * (ubyte_f32<2>(w0) - 8.0f);
+    v[3] = d * (ubyte_f32<3>(w0) - 8.0f);
+    v[4] = d * (ubyte_f32<0>(w1) - 8.0f);
+    v[5] = d * (ubyte_f32<1>(w1) - 8.0f);
+    v[6] = d * (ubyte_f32<2>(w1) - 8.0f);
+    v[7] = d * (ubyte_f32<3>(w1) - 8.0f);
+}
+
+// Q5_0, 8 outputs (block 2-byte aligned): q = nibble + 16·(bit e of qh), value
+// d·(q − 16).  qh is read as two 2-byte halves (the block start is only
+// 2-byte aligned).
+__device__ __forceinline__ void decode_q50(const uint8_t *blk, uint32_t e0, float v[8]) {
+    const float d = f16_bits_to_f32(lds_u16(blk));
+    const uint32_t hb = lds_u32_a2(blk + 2) >> e0;
+    uint32_t w0, w1;
+    nibbles8(blk + 6, e0, w0, w1);
+    w0 = opaque(w0 | spread4_to_bit4(hb & 15));
+    w1 = opaque(w1 | spread4_to_bit4((hb >> 4) & 15));
+    v[0] = d * (ubyte_f32<0>(w0) - 16.0f);
+    v[1] = d * (ubyte_f32<1>(w0) - 16.0f);
+    v[2] = d * (ubyte_f32<2>(w0) - 16.0f);
+    v[3] = d * (ubyte_f32<3>(w0) - 16.0f);
+    v[4] = d * (ubyte_f32<0>(w1) - 16.0f);
+    v[5] = d * (ubyte_f32<1>(w1) - 16.0f);
+    v[6] = d * (ubyte_f32<2>(w1) - 16.0f);
+    v[7] = d * (ubyte_f32<3>(w1) - 16.0f);
+}
+
+// Q5_1, 8 outputs: q as Q5_0, value fl32(d·q + m) (d·q exact, one rounding).
+__device__ __forceinline__ void decode_q51(const uint8_t *blk, uint32_t e0, float v[8]) {
+    const float d = f16_bits_to_f32(lds_u16(blk)), m = f16_bits_to_f32(lds_u16(blk + 2));
+    const uint32_t hb = lds_u32_a2(blk + 4) >> e0;
+    uint32_t w0, w1;
+    nibbles8(blk + 8, e0, w0, w1);
+    w0 = opaque(w0 | spread4_to_bit4(hb & 15));
+    w1 = opaque(w1 | spread4_to_bit4((hb >> 4) & 15));
+    v[0] = __builtin_fmaf(d, ubyte_f32<0>(w0), m);
+    v[1] = __builtin_fmaf(d, ubyte_f32<1>(w0), m);
+    v[2] = __builtin_fmaf(d, ubyte_f32<2>(w0), m);
+    v[3] = __builtin_fmaf(d, ubyte_f32<3>(w0), m);
+    v[4] = __builtin_fmaf(d, ubyte_f32<0>(w1), m);
+    v[5] = __builtin_fmaf(d, ubyte_f32<1>(w1), m);
+    v[6] = __builtin_fmaf(d, ubyte_f32<2>(w1), m);
+    v[7] = __builtin_fmaf(d, ubyte_f32<3>(w1), m);
+}
+
+// Q5_K, 8 outputs of the block at `blk` (16-byte aligned): as Q4_K, plus bit j
+// (the sub-block) of qh[l] as the 16s bit of element l of sub-block j.
+__device__ __forceinline__ void decode_q5k(const uint8_t *blk, uint32_t e0, float v[8]) {
+    const u32x4 h = *(const u32x4 *)blk;
+    const uint32_t c = e0 >> 6, r = e0 & 63, j = e0 >> 5, l0 = r & 31;
+    const u32x2 qq = *(const u32x2 *)(blk + 48 + 32 * c + l0);
+    const u32x2 hh = *(const u32x2 *)(blk + 16 + l0);
+    const uint32_t sh = 8 * (j & 3);
+    const uint32_t s_lo = (h.y >> sh) & 0xFF, s_mid = (h.z >> sh) & 0xFF, s_hi = (h.w >> sh) & 0xFF;
+    const uint32_t sc = j < 4 ? (s_lo & 63) : ((s_hi & 15) | ((s_lo >> 6) << 4));
+    const uint32_t m = j < 4 ? (s_mid & 63) : ((s_hi >> 4) | ((s_mid >> 6) << 4));
+    const float A = f16_bits_to_f32(h.x) * (float)sc;
+    const float C = f16_bits_to_f32(h.x >> 16) * (float)m;
+    const uint32_t n4 = (r >= 32) ? 4 : 0;
+    const uint32_t w0 = opaque(((qq.x >> n4) & 0x0F0F0F0Fu) | (((hh.x >> j) & 0x01010101u) << 4));
+    const uint32_t w1 = opaque(((qq.y >> n4) & 0x0F0F0F0Fu) | (((hh.y >> j) & 0x01010101u) << 4));
+    // A·q is exact (≤ 22 bits), so one fused rounding equals fl32(A·q − C)
+    v[0] = __builtin_fmaf(A, ubyte_f32<0>(w0), -C);
+    v[1] = __builtin_fmaf(A, ubyte_f32<1>(w0), -C);
+    v[2] = __builtin_fmaf(A, ubyte_f32<2>(w0), -C);
+    v[3] = __builtin_fmaf(A, ubyte_f32<3>(w0), -C);
+    v[4] = __builtin_fmaf(A, ubyte_f32<0>(w1), -C);
+    v[5] = __builtin_fmaf(A, ubyte_f32<1>(w1), -C);
+    v[6] = __builtin_fmaf(A, ubyte_f32<2>(w1), -C);
+    v[7] = __builtin_fmaf(A, ubyte_f32<3>(w1), -C);
+}
+
 // Shape of one decode: the matrix's blocks, its cache, and how the groups of
 // 16 KiB of output (data groups first, then the pad-column groups) cover it.
 struct DequantJob {
@@ -133,7 +238,10 @@ struct DequantJob {
 // LDS stage large enough for any format's group
 constexpr uint32_t kStageMax =
     stage_bytes<kFmtQ8_0>() > stage_bytes<kFmtQ6_K>() ? stage_bytes<kFmtQ8_0>() : stage_bytes<kFmtQ6_K>();
-static_assert(stage_bytes<kFmtQ4_K>() <= kStageMax, "stage size");
+static_assert(stage_bytes<kFmtQ4_K>() <= kStageMax && stage_bytes<kFmtQ5_K>() <= kStageMax &&
+                  stage_bytes<kFmtQ4_0>() <= kStageMax && stage_bytes<kFmtQ5_0>() <= kStageMax &&
+                  stage_bytes<kFmtQ5_1>() <= kStageMax,
+              "stage size");
 
 // Workgroup `grp` of a job decodes group_blocks<FMT>() consecutive blocks
 // (16 KiB of f16 output).  Phase 1: the blocks' bytes — a contiguous span of
@@ -193,9 +301,14 @@ __device__ __forceinline__ void decode_group(const DequantJob &j, uint32_t grp, 
         const uint32_t g = g0 + gl;
         const uint32_t row = g / j.nb, kb = g - row * j.nb;
         float v[8];
-        if constexpr (FMT == kFmtQ4_K) decode_q4k(bytes + gl * BB, e0, v);
-        else if constexpr (FMT == kFmtQ6_K) decode_q6k(bytes + gl * BB, e0, v);
-        else decode_q80(bytes + gl * BB, e0, v);
+        const uint8_t *blk = bytes + gl * BB;
+        if constexpr (FMT == kFmtQ4_K) decode_q4k(blk, e0, v);
+        else if constexpr (FMT == kFmtQ6_K) decode_q6k(blk, e0, v);
+        else if constexpr (FMT == kFmtQ8_0) decode_q80(blk, e0, v);
+        else if constexpr (FMT == kFmtQ4_0) decode_q40(blk, e0, v);
+        else if constexpr (FMT == kFmtQ5_0) decode_q50(blk, e0, v);
+        else if constexpr (FMT == kFmtQ5_1) decode_q51(blk, e0, v);
+        else decode_q5k(blk, e0, v);
         store8(j.out + (size_t)row * j.ld + kb * BE + e0, v);
     }
 }
@@ -226,6 +339,10 @@ __global__ __launch_bounds__(kThreads) void dequant_batch_kernel(DequantBatch b)
     switch (j.fmt) {
     case kFmtQ4_K: decode_group<kFmtQ4_K>(j, grp, stage); break;
     case kFmtQ6_K: decode_group<kFmtQ6_K>(j, grp, stage); break;
+    case kFmtQ5_K: decode_group<kFmtQ5_K>(j, grp, stage); break;
+    case kFmtQ4_0: decode_group<kFmtQ4_0>(j, grp, stage); break;
+    case kFmtQ5_0: decode_group<kFmtQ5_0>(j, grp, stage); break;
+    case kFmtQ5_1: decode_group<kFmtQ5_1>(j, grp, stage); break;
     default: decode_group<kFmtQ8_0>(j, grp, stage); break;
     }
 }
@@ -252,6 +369,10 @@ DequantJob job_for(int fmt, const void *wq, int N, int K, uint16_t *w16, int ld)
     switch (fmt) {
     case kFmtQ4_K: return make_job<kFmtQ4_K>(wq, N, K, w16, ld);
     case kFmtQ6_K: return make_job<kFmtQ6_K>(wq, N, K, w16, ld);
+    case kFmtQ5_K: return make_job<kFmtQ5_K>(wq, N, K, w16, ld);
+    case kFmtQ4_0: return make_job<kFmtQ4_0>(wq, N, K, w16, ld);
+    case kFmtQ5_0: return make_job<kFmtQ5_0>(wq, N, K, w16, ld);
+    case kFmtQ5_1: return make_job<kFmtQ5_1>(wq, N, K, w16, ld);
     default: return make_job<kFmtQ8_0>(wq, N, K, w16, ld);
     }
 }
@@ -265,6 +386,10 @@ hipError_t launch_dequant(int fmt, const void *wq, int N, int K, uint16_t *w16, 
     switch (fmt) {
     case kFmtQ4_K: hipLaunchKernelGGL(dequant_kernel<kFmtQ4_K>, grid, block, 0, stream, j); break;
     case kFmtQ6_K: hipLaunchKernelGGL(dequant_kernel<kFmtQ6_K>, grid, block, 0, stream, j); break;
+    case kFmtQ5_K: hipLaunchKernelGGL(dequant_kernel<kFmtQ5_K>, grid, block, 0, stream, j); break;
+    case kFmtQ4_0: hipLaunchKernelGGL(dequant_kernel<kFmtQ4_0>, grid, block, 0, stream, j); break;
+    case kFmtQ5_0: hipLaunchKernelGGL(dequant_kernel<kFmtQ5_0>, grid, block, 0, stream, j); break;
+    case kFmtQ5_1: hipLaunchKernelGGL(dequant_kernel<kFmtQ5_1>, grid, block, 0, stream, j); break;
     default: hipLaunchKernelGGL(dequant_kernel<kFmtQ8_0>, grid, block, 0, stream, j); break;
     }
     return hipGetLastError();

@@ -399,12 +399,208 @@ struct Q80Loader {
     }
 };
 
+// The 16s bits of 4 consecutive elements, bits 0..3 of b, moved to bit 4 of
+// bytes 0..3 (b·(1 + 2^7 + 2^14 + 2^21) puts bit i at bit 8i; the partial
+// products do not overlap).
+__device__ __forceinline__ uint32_t spread4_to_bit4(uint32_t b) {
+    return ((b * 0x00204081u) & 0x01010101u) << 4;
+}
+
+// ---------------------------------------------------------------------------
+// Q4_0 / Q5_0 / Q5_1 B loader (32-element blocks of 18 / 22 / 24 bytes).  A
+// k-step is two blocks per row; thread (row, p) takes block 2·step + p, read
+// as the aligned dwords covering it (Q4_0 and Q5_0 blocks are only 2-byte
+// aligned — the Q5_0 qh word at byte 2 included, the misalignment the pages
+// report — so every field is re-assembled with v_alignbyte).  Element j of a
+// block: nibble j % 16 (low for j < 16), plus for Q5_x bit j of qh as 16s bit.
+// ---------------------------------------------------------------------------
+template <int ROWS, int FMT>
+struct Q32Loader {
+    static constexpr int NPART = ROWS * 2 / kThreads;
+    static constexpr uint32_t BB = FMT == kFmtQ4_0 ? 18 : FMT == kFmtQ5_0 ? 22 : 24;
+    static constexpr uint32_t QH = FMT == kFmtQ5_1 ? 4 : 2;    // qh offset (Q5_x)
+    static constexpr uint32_t QS = FMT == kFmtQ4_0 ? 2 : FMT == kFmtQ5_0 ? 6 : 8;
+    // dwords held: the block plus up to 2 lead bytes needs 5 (Q4_0) or 6; one
+    // more (zero) lets dw<T> read its upper neighbour for every field
+    static constexpr int NW = 7;
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t roff[NPART];
+    uint32_t w[2][NPART][NW], sh[2][NPART];
+    int nb, blk[2];
+    bool live_[2];
+
+    __device__ void init(const uint8_t *W, int64_t row_bytes, int n0, int rows_valid, int K) {
+        nb = K >> 5;
+        const int64_t start = (int64_t)n0 * row_bytes;
+        const uint32_t shift0 = (uint32_t)(((uintptr_t)W + start) & 15);
+        const int64_t extent = shift0 + (int64_t)rows_valid * row_bytes;
+        rs = make_rsrc(W + start - shift0, (uint32_t)((extent + 3) & ~(int64_t)3));
+#pragma unroll
+        for (int i = 0; i < NPART; ++i) {
+            const int r = (i * kThreads + (int)threadIdx.x) >> 1;
+            roff[i] = shift0 + (uint32_t)(r * row_bytes);
+        }
+    }
+    __device__ __forceinline__ void begin(int set, int k0, bool live) {
+        blk[set] = (k0 >> 5) + ((int)threadIdx.x & 1);
+        live_[set] = live && blk[set] < nb;
+    }
+    __device__ __forceinline__ void load(int set, int i) {
+        const uint32_t o = roff[i] + (uint32_t)blk[set] * BB;
+        sh[set][i] = o & 3;                       // 0 or 2: blocks are 2-byte aligned
+        const uint32_t a = live_[set] ? (o & ~3u) : kOOB;
+        const u32x4 v0 = buf_load16(rs, a);
+        uint32_t *q = w[set][i];
+        q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
+        if constexpr (FMT == kFmtQ4_0) {          // 18 + 2 bytes: 5 dwords
+            q[4] = buf_load4(rs, a + 16);
+            q[5] = 0;
+        } else {                                  // 22 or 24 (+ 2) bytes: 6 dwords
+            const uint32_t t = a + 16;
+            q[4] = buf_load4(rs, t);
+            q[5] = buf_load4(rs, t + 4);
+        }
+        q[6] = 0;
+    }
+    // dword of the block at even byte offset T (compile-time), from the raw window
+    template <uint32_t T>
+    __device__ __forceinline__ uint32_t dw(const uint32_t *q, uint32_t s) const {
+        const uint32_t lo = __builtin_amdgcn_alignbyte(q[T / 4 + 1], q[T / 4], s);
+        if constexpr (T % 4 == 0) {
+            return lo;
+        } else {
+            const uint32_t hi = __builtin_amdgcn_alignbyte(q[T / 4 + 2], q[T / 4 + 1], s);
+            return __builtin_amdgcn_alignbyte(hi, lo, 2);
+        }
+    }
+    __device__ __forceinline__ void store(int set, int i, u32x4 *lds) const {
+        const int p = (int)threadIdx.x & 1;
+        const int r = (i * kThreads + (int)threadIdx.x) >> 1;
+        const uint32_t *q = w[set][i];
+        const uint32_t s = sh[set][i];
+        const uint32_t h0 = dw<0>(q, s);
+        const float d = f16_bits_to_f32(h0);
+        const uint32_t n0 = dw<QS>(q, s), n1 = dw<QS + 4>(q, s), n2 = dw<QS + 8>(q, s),
+                       n3 = dw<QS + 12>(q, s);
+        uint32_t qh = 0;
+        if constexpr (FMT != kFmtQ4_0) qh = dw<QH>(q, s);
+        u32x4 *row = lds + r * 8;
+        const int sw = swz<8>(r);
+        const uint32_t L = 0x0F0F0F0Fu;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // elements 8c .. 8c+7: bytes (8c) % 16 .. +7 of the nibble plane
+            const uint32_t a0 = c & 1 ? n2 : n0, a1 = c & 1 ? n3 : n1;
+            uint32_t w0 = c < 2 ? (a0 & L) : ((a0 >> 4) & L);
+            uint32_t w1 = c < 2 ? (a1 & L) : ((a1 >> 4) & L);
+            u32x4 v;
+            if constexpr (FMT == kFmtQ4_0) {
+                w0 = opaque(w0);
+                w1 = opaque(w1);
+                v = pack8(d * (ubyte_f32<0>(w0) - 8.0f), d * (ubyte_f32<1>(w0) - 8.0f),
+                          d * (ubyte_f32<2>(w0) - 8.0f), d * (ubyte_f32<3>(w0) - 8.0f),
+                          d * (ubyte_f32<0>(w1) - 8.0f), d * (ubyte_f32<1>(w1) - 8.0f),
+                          d * (ubyte_f32<2>(w1) - 8.0f), d * (ubyte_f32<3>(w1) - 8.0f));
+            } else {
+                const uint32_t hb = qh >> (8 * c);
+                w0 = opaque(w0 | spread4_to_bit4(hb & 15));
+                w1 = opaque(w1 | spread4_to_bit4((hb >> 4) & 15));
+                if constexpr (FMT == kFmtQ5_0) {
+                    v = pack8(d * (ubyte_f32<0>(w0) - 16.0f), d * (ubyte_f32<1>(w0) - 16.0f),
+                              d * (ubyte_f32<2>(w0) - 16.0f), d * (ubyte_f32<3>(w0) - 16.0f),
+                              d * (ubyte_f32<0>(w1) - 16.0f), d * (ubyte_f32<1>(w1) - 16.0f),
+                              d * (ubyte_f32<2>(w1) - 16.0f), d * (ubyte_f32<3>(w1) - 16.0f));
+                } else {
+                    const float m = f16_bits_to_f32(h0 >> 16);
+                    v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), m), __builtin_fmaf(d, ubyte_f32<1>(w0), m),
+                              __builtin_fmaf(d, ubyte_f32<2>(w0), m), __builtin_fmaf(d, ubyte_f32<3>(w0), m),
+                              __builtin_fmaf(d, ubyte_f32<0>(w1), m), __builtin_fmaf(d, ubyte_f32<1>(w1), m),
+                              __builtin_fmaf(d, ubyte_f32<2>(w1), m), __builtin_fmaf(d, ubyte_f32<3>(w1), m));
+                }
+            }
+            row[(4 * p + c) ^ sw] = v;
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Q5_K B loader: Q4_K's, plus the 16 qh bytes l = 16p .. 16p+15 of the thread:
+// bit j of qh[l] is the 16s bit of element l of sub-block j.  Blocks are 176
+// bytes, so every load is 16-byte aligned.
+// ---------------------------------------------------------------------------
+template <int ROWS>
+struct Q5KLoader {
+    static constexpr int NPART = ROWS * 2 / kThreads;
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t roff[NPART];
+    uint32_t obase[2];
+    int c4[2];
+    u32x4 hdr[2][NPART], qh[2][NPART], qs[2][NPART];
+
+    __device__ void init(const uint8_t *W, int64_t row_bytes, int n0, int rows_valid, int) {
+        rs = make_rsrc(W + (int64_t)n0 * row_bytes, (uint32_t)(rows_valid * row_bytes));
+#pragma unroll
+        for (int i = 0; i < NPART; ++i) {
+            const int r = (i * kThreads + (int)threadIdx.x) >> 1;
+            roff[i] = (uint32_t)(r * row_bytes);
+        }
+    }
+    __device__ __forceinline__ void begin(int set, int k0, bool live) {
+        c4[set] = (k0 >> 6) & 3;
+        obase[set] = live ? (uint32_t)(k0 >> 8) * 176u : kOOB;
+    }
+    __device__ __forceinline__ void load(int set, int i) {
+        const uint32_t o = roff[i] + obase[set], p = (int)threadIdx.x & 1;
+        hdr[set][i] = buf_load16(rs, o);
+        qh[set][i] = buf_load16(rs, o + 16 + 16 * p);
+        qs[set][i] = buf_load16(rs, o + 48 + 32 * c4[set] + 16 * p);
+    }
+    __device__ __forceinline__ void store(int set, int i, u32x4 *lds) const {
+        const int p = (int)threadIdx.x & 1, c = c4[set];
+        const int r = (i * kThreads + (int)threadIdx.x) >> 1;
+        const u32x4 h = hdr[set][i];
+        uint32_t sc0, m0, sc1, m1;
+        if (c < 2) {
+            const int s0 = 16 * c, s1 = 16 * c + 8;
+            sc0 = (h.y >> s0) & 63;
+            m0 = (h.z >> s0) & 63;
+            sc1 = (h.y >> s1) & 63;
+            m1 = (h.z >> s1) & 63;
+        } else {
+            const int s0 = 16 * (c - 2), s1 = s0 + 8;
+            sc0 = ((h.w >> s0) & 15) | (((h.y >> (s0 + 6)) & 3) << 4);
+            m0 = ((h.w >> (s0 + 4)) & 15) | (((h.z >> (s0 + 6)) & 3) << 4);
+            sc1 = ((h.w >> s1) & 15) | (((h.y >> (s1 + 6)) & 3) << 4);
+            m1 = ((h.w >> (s1 + 4)) & 15) | (((h.z >> (s1 + 6)) & 3) << 4);
+        }
+        const float d = f16_bits_to_f32(h.x), dmin = f16_bits_to_f32(h.x >> 16);
+        const float A0 = d * (float)sc0, C0 = dmin * (float)m0;
+        const float A1 = d * (float)sc1, C1 = dmin * (float)m1;
+        const u32x4 q = qs[set][i], hq = qh[set][i];
+        const uint32_t L = 0x0F0F0F0Fu, B = 0x01010101u, j0 = 2 * c, j1 = 2 * c + 1;
+        u32x4 *row = lds + r * 8;
+        const int sw = swz<8>(r);
+        row[(2 * p) ^ sw] = q4k_chunk((q.x & L) | (((hq.x >> j0) & B) << 4),
+                                      (q.y & L) | (((hq.y >> j0) & B) << 4), A0, C0);
+        row[(2 * p + 1) ^ sw] = q4k_chunk((q.z & L) | (((hq.z >> j0) & B) << 4),
+                                          (q.w & L) | (((hq.w >> j0) & B) << 4), A0, C0);
+        row[(4 + 2 * p) ^ sw] = q4k_chunk(((q.x >> 4) & L) | (((hq.x >> j1) & B) << 4),
+                                          ((q.y >> 4) & L) | (((hq.y >> j1) & B) << 4), A1, C1);
+        row[(5 + 2 * p) ^ sw] = q4k_chunk(((q.z >> 4) & L) | (((hq.z >> j1) & B) << 4),
+                                          ((q.w >> 4) & L) | (((hq.w >> j1) & B) << 4), A1, C1);
+    }
+};
+
 template <int ROWS, int FMT>
 struct BLoaderFor;
 template <int ROWS> struct BLoaderFor<ROWS, kFmtF16> { typedef F16Loader<ROWS> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ4_K> { typedef Q4KLoader<ROWS> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ6_K> { typedef Q6KLoader<ROWS> T; };
 template <int ROWS> struct BLoaderFor<ROWS, kFmtQ8_0> { typedef Q80Loader<ROWS> T; };
+template <int ROWS> struct BLoaderFor<ROWS, kFmtQ4_0> { typedef Q32Loader<ROWS, kFmtQ4_0> T; };
+template <int ROWS> struct BLoaderFor<ROWS, kFmtQ5_0> { typedef Q32Loader<ROWS, kFmtQ5_0> T; };
+template <int ROWS> struct BLoaderFor<ROWS, kFmtQ5_1> { typedef Q32Loader<ROWS, kFmtQ5_1> T; };
+template <int ROWS> struct BLoaderFor<ROWS, kFmtQ5_K> { typedef Q5KLoader<ROWS> T; };
 
 // Stage boundary: every LDS access of this wave done, then meet the other
 // waves.  The barrier is an asm statement with a memory clobber, so the
@@ -773,6 +969,10 @@ hipError_t launch_gemm(int fmt, const uint16_t *X, int ldx, const void *W, int64
     case kFmtQ4_K: e = launch_fmt<kFmtQ4_K>(a, plan.bm, plan.bn, grid, stream); break;
     case kFmtQ6_K: e = launch_fmt<kFmtQ6_K>(a, plan.bm, plan.bn, grid, stream); break;
     case kFmtQ8_0: e = launch_fmt<kFmtQ8_0>(a, plan.bm, plan.bn, grid, stream); break;
+    case kFmtQ4_0: e = launch_fmt<kFmtQ4_0>(a, plan.bm, plan.bn, grid, stream); break;
+    case kFmtQ5_0: e = launch_fmt<kFmtQ5_0>(a, plan.bm, plan.bn, grid, stream); break;
+    case kFmtQ5_1: e = launch_fmt<kFmtQ5_1>(a, plan.bm, plan.bn, grid, stream); break;
+    case kFmtQ5_K: e = launch_fmt<kFmtQ5_K>(a, plan.bm, plan.bn, grid, stream); break;
     default: e = launch_fmt<kFmtF16>(a, plan.bm, plan.bn, grid, stream); break;
     }
     if (e != hipSuccess || plan.split == 1) return e;

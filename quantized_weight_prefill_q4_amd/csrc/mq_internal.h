@@ -7,15 +7,32 @@
 namespace mq {
 
 constexpr int kFmtF16 = 0;  // the f16-cache operand of the GEMM
+constexpr int kFmtQ4_0 = 2;
+constexpr int kFmtQ5_0 = 6;
+constexpr int kFmtQ5_1 = 7;
 constexpr int kFmtQ8_0 = 8;
 constexpr int kFmtQ4_K = 12;
+constexpr int kFmtQ5_K = 13;
 constexpr int kFmtQ6_K = 14;
 
 inline int block_elems(int fmt) {
-    return fmt == kFmtQ8_0 ? 32 : (fmt == kFmtQ4_K || fmt == kFmtQ6_K) ? 256 : -1;
+    switch (fmt) {
+    case kFmtQ4_0: case kFmtQ5_0: case kFmtQ5_1: case kFmtQ8_0: return 32;
+    case kFmtQ4_K: case kFmtQ5_K: case kFmtQ6_K: return 256;
+    default: return -1;
+    }
 }
 inline int block_bytes(int fmt) {
-    return fmt == kFmtQ8_0 ? 34 : fmt == kFmtQ4_K ? 144 : fmt == kFmtQ6_K ? 210 : -1;
+    switch (fmt) {
+    case kFmtQ4_0: return 18;
+    case kFmtQ5_0: return 22;
+    case kFmtQ5_1: return 24;
+    case kFmtQ8_0: return 34;
+    case kFmtQ4_K: return 144;
+    case kFmtQ5_K: return 176;
+    case kFmtQ6_K: return 210;
+    default: return -1;
+    }
 }
 
 // Decode launcher (arguments already validated).

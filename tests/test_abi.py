@@ -46,9 +46,19 @@ def test_format_tables(L):
     assert (L.mq_block_elems(12), L.mq_block_bytes(12)) == (256, 144)
     assert (L.mq_block_elems(14), L.mq_block_bytes(14)) == (256, 210)
     assert (L.mq_block_elems(8), L.mq_block_bytes(8)) == (32, 34)
-    assert L.mq_block_elems(2) == _lib.MQ_ERR_FORMAT
-    for fmt, K in ((12, 3584), (14, 18944), (8, 4096), (12, 256), (8, 32)):
+    # 2 + 16, 2 + 4 + 16, 2 + 2 + 4 + 16, and Q4_K's 144 + 32 bytes of qh
+    assert (L.mq_block_elems(2), L.mq_block_bytes(2)) == (32, 18)
+    assert (L.mq_block_elems(6), L.mq_block_bytes(6)) == (32, 22)
+    assert (L.mq_block_elems(7), L.mq_block_bytes(7)) == (32, 24)
+    assert (L.mq_block_elems(13), L.mq_block_bytes(13)) == (256, 176)
+    for unknown in (0, 1, 3, 4, 5, 9, 10, 11, 15, 99):
+        assert L.mq_block_elems(unknown) == _lib.MQ_ERR_FORMAT
+        assert L.mq_block_bytes(unknown) == _lib.MQ_ERR_FORMAT
+    for fmt, K in ((12, 3584), (14, 18944), (8, 4096), (12, 256), (8, 32), (2, 4096),
+                   (6, 4096), (7, 32), (13, 3584), (13, 256)):
         assert L.mq_row_bytes(fmt, K) == oracle_row_bytes(fmt, K)
+    assert L.mq_row_bytes(6, 48) == _lib.MQ_ERR_SHAPE
+    assert L.mq_row_bytes(13, 3200) == _lib.MQ_ERR_SHAPE
     assert L.mq_row_bytes(12, 100) == _lib.MQ_ERR_SHAPE
     assert L.mq_row_bytes(99, 256) == _lib.MQ_ERR_FORMAT
 
@@ -145,6 +155,9 @@ def test_workspace_planning(L):
     # tiles: 4 rounds + 160 tiles -> no split
     assert L.mq_gemm_workspace_bytes(12, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
     assert L.mq_gemm_workspace_bytes(14, 2048, 18944, 3584, 0) == 0
+    # every other weight format takes the 256 x 256 fused tiles too
+    for fmt in (2, 6, 7, 8, 13):
+        assert L.mq_gemm_workspace_bytes(fmt, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
     # q/o: 224 tiles of 256 x 128, one partial round that a split cannot double
     assert L.mq_gemm_workspace_bytes(0, 2048, 3584, 3584, 0) == 0
     assert L.mq_gemm_workspace_bytes(0, 64, 512, 512, 1) == 0
