@@ -45,7 +45,8 @@ ROOFLINE_KERNEL = "gemm_kernel<256, 256, f16> + splitk_reduce (mq_gemm_f16cache,
 # by a plain copy of known size) with the hash of the GEMM source it was taken
 # on; reported only while the source is unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_f16cache_gate_7b_m2048_traffic.md")
-GEMM_SOURCES = ("quantized_weight_prefill_q4_amd/csrc/gemm.hip",
+GEMM_SOURCES = ("quantized_weight_prefill_q4_amd/csrc/gemm_kernel.h",
+                "quantized_weight_prefill_q4_amd/csrc/gemm.hip",
                 "quantized_weight_prefill_q4_amd/csrc/mq_device.h")
 
 
@@ -65,6 +66,10 @@ def parse():
     p.add_argument("--grouped-steps", type=int, default=5,
                    help="steps of the grouped forward (q|k|v, gate|up as one GEMM each); 0 = skip")
     p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-formats", action="store_true",
+                   help="skip the per-format decode / fused table")
+    p.add_argument("--no-xf32", action="store_true",
+                   help="skip the f32-activation table")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="token rows of the oracle sample")
@@ -266,6 +271,117 @@ def sweep(torch, mq, dev, log_rows):
         out[name] = {"crossover_M": cross, "by_M": {m: res[m] for m in sorted(res)}}
         del caches, qs, cache0, q0
         torch.cuda.empty_cache()
+    return out
+
+
+def _median_us(torch, fn, reps, warm=2):
+    """Median duration (us) of fn(r) over reps calls after warm untimed ones."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for r in range(reps + warm):
+        if r >= warm:
+            evs[r - warm].record()
+        fn(r)
+    evs[reps].record()
+    torch.cuda.synchronize()
+    return statistics.median(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(reps))
+
+
+def formats_table(torch, mq, dev, log_rows):
+    """Every weight format on one shape (N = 14336, K = 4096, the Llama-3.1-8B
+    gate/up projection): load-time decode GB/s (quantized bytes read + f16
+    cache written) and the fused GEMM at M = 128 and 2048, beside the cache
+    GEMM on the same shape.  Weight copies rotate over > 512 MB."""
+    N, K = 14336, 4096
+    x = synth.activations_device(6100, 2048, K, dev)
+    out = {}
+    cache_us = {}
+    for fi, (fname, fmt) in enumerate(sorted(mq.FORMATS.items(), key=lambda kv: kv[1])):
+        q0 = synth.weights_device(fmt, 6200 + fi, N, K, dev)
+        nq = max(3, -(-512 * 2 ** 20 // q0.numel()))
+        qs = [q0] + [q0.clone() for _ in range(nq - 1)]
+        ld = mq.cache_ld(K)
+        caches = [torch.empty((N, ld), dtype=torch.float16, device=dev) for _ in range(5)]
+        t_deq = _median_us(torch, lambda r: mq.dequant_to_f16(qs[r % nq], fmt, N, K,
+                                                              out=caches[r % 5]), 12)
+        rec = {"quant_bytes": int(q0.numel()),
+               "dequant_us": round(t_deq, 2),
+               "dequant_gbs": round((q0.numel() + 2 * N * ld) / t_deq / 1e3, 1)}
+        for M in (128, 2048):
+            xm = x[:M]
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(1, mq.workspace_bytes(fmt, M, N, K) // 4), dtype=torch.float32,
+                             device=dev)
+            t = _median_us(torch, lambda r: mq.gemm_fused(xm, qs[r % nq], fmt, N, K, out=y, ws=ws), 12)
+            rec[f"fused_m{M}_us"] = round(t, 2)
+            rec[f"fused_m{M}_tflops"] = round(2.0 * M * N * K / t / 1e6, 1)
+            if M not in cache_us:
+                wsc = torch.empty(max(1, mq.workspace_bytes(0, M, N, K) // 4), dtype=torch.float32,
+                                  device=dev)
+                cache_us[M] = _median_us(torch, lambda r: mq.gemm_f16cache(
+                    xm, caches[r % 5], K, out=y, ws=wsc), 12)
+        out[fname] = rec
+        log_rows.append(f"  {fname:5s} {rec['quant_bytes'] / 2 ** 20:6.1f} MiB  decode {t_deq:7.1f} us "
+                        f"{rec['dequant_gbs']:6.0f} GB/s   fused M=128 {rec['fused_m128_us']:7.1f} us "
+                        f"({rec['fused_m128_tflops']:6.1f} TF/s)  M=2048 {rec['fused_m2048_us']:7.1f} us "
+                        f"({rec['fused_m2048_tflops']:6.1f} TF/s)")
+        del qs, q0, caches
+        torch.cuda.empty_cache()
+    out["cache_gemm"] = {f"m{M}_us": round(t, 2) for M, t in cache_us.items()}
+    log_rows.append("  cache GEMM on the same shape: " +
+                    ", ".join(f"M={M} {t:.1f} us ({2.0 * M * N * K / t / 1e6:.1f} TF/s)"
+                              for M, t in cache_us.items()))
+    return out
+
+
+def xf32_table(torch, mq, dev, log_rows):
+    """f32 activations on the Llama-3.1-8B gate/up shape (N = 14336, K = 4096),
+    for the f16 cache and the fused Q4_K GEMM: the f32-activation kernel
+    (rounds X to f16 while staging its tile) against the standalone convert
+    followed by the f16-activation kernel, per M; the f16-activation kernel
+    alone for reference.  Weight copies rotate over > 512 MB."""
+    N, K = 14336, 4096
+    fmt = mq.FORMATS["q4_k"]
+    q0 = synth.weights_device(fmt, 6300, N, K, dev)
+    nq = max(3, -(-512 * 2 ** 20 // q0.numel()))
+    qs = [q0] + [q0.clone() for _ in range(nq - 1)]
+    caches = [mq.dequant_to_f16(q0, fmt, N, K)] + [None] * 4
+    for i in range(1, 5):
+        caches[i] = caches[0].clone()
+    g = torch.Generator(device=dev)
+    g.manual_seed(6301)
+    x32 = torch.randn((2048, K), generator=g, device=dev, dtype=torch.float32)
+    x16 = torch.empty((2048, K), dtype=torch.float16, device=dev)
+    out = {}
+    for M in (128, 512, 2048):
+        xm32, xm16 = x32[:M], x16[:M]
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        rec = {"convert_us": round(_median_us(torch, lambda r: mq.convert_f32_to_f16(xm32, out=xm16), 12), 2)}
+        for path in ("cache", "fused"):
+            def gemm(x, r, path=path):
+                ws = wss[(path, x.dtype)]
+                if path == "cache":
+                    mq.gemm_f16cache(x, caches[r % 5], K, out=y, ws=ws)
+                else:
+                    mq.gemm_fused(x, qs[r % nq], fmt, N, K, out=y, ws=ws)
+            wss = {}
+            for dt, xf in ((torch.float16, False), (torch.float32, True)):
+                b = mq.workspace_bytes(0 if path == "cache" else fmt, M, N, K, 0, x_f32=xf)
+                wss[(path, dt)] = (torch.empty(b // 4, dtype=torch.float32, device=dev)
+                                   if b else None)
+            t16 = _median_us(torch, lambda r: gemm(xm16, r), 12)
+            t32 = _median_us(torch, lambda r: gemm(xm32, r), 12)
+            tcv = _median_us(torch, lambda r: (mq.convert_f32_to_f16(xm32, out=xm16), gemm(xm16, r)), 12)
+            rec[path] = {"x16_us": round(t16, 2), "xf32_us": round(t32, 2),
+                         "convert_then_x16_us": round(tcv, 2),
+                         "xf32_tflops": round(2.0 * M * N * K / t32 / 1e6, 1)}
+            log_rows.append(f"  {path:5s} M={M:5d}  f16 X {t16:8.1f} us   f32 X in-kernel {t32:8.1f} us"
+                            f"   convert + f16 X {tcv:8.1f} us   (convert alone {rec['convert_us']:.1f} us)")
+        out[M] = rec
+    for path in ("cache", "fused"):
+        wins = [M for M in sorted(out) if out[M][path]["convert_then_x16_us"] < out[M][path]["xf32_us"]]
+        out[f"{path}_convert_first_from_M"] = wins[0] if wins else None
+    del qs, caches, x32, x16
+    torch.cuda.empty_cache()
     return out
 
 
@@ -537,6 +653,24 @@ def main():
         log("  crossover M (smallest M where the cache GEMM is faster): " +
             ", ".join(f"{k}: {v['crossover_M']}" for k, v in cross.items()))
 
+    # -- every weight format on one shape ------------------------------------------------
+    fmts = None
+    if not args.no_formats:
+        rows = []
+        fmts = formats_table(torch, mq, dev, rows)
+        log("[bench] weight formats on 14336x4096 (decode; fused GEMM), median of 12 calls:")
+        for r in rows:
+            log(r)
+
+    # -- f32 activations ----------------------------------------------------------------
+    xf32 = None
+    if not args.no_xf32:
+        rows = []
+        xf32 = xf32_table(torch, mq, dev, rows)
+        log("[bench] f32 activations on 14336x4096 (cache and fused Q4_K), median of 12 calls:")
+        for r in rows:
+            log(r)
+
     # -- CPU oracle baseline -------------------------------------------------------------
     cpu = None
     if not args.no_cpu:
@@ -586,6 +720,8 @@ def main():
         "fused": fused,
         "grouped_forward": grouped,
         "crossover": cross,
+        "formats": fmts,
+        "xf32": xf32,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -82,7 +82,8 @@ enum {
     MQ_ERR_NULL = -1,      /* a required pointer is NULL */
     MQ_ERR_FORMAT = -2,    /* unknown weight format */
     MQ_ERR_SHAPE = -3,     /* M, N or K <= 0 or too large, or K not a multiple of the block */
-    MQ_ERR_LD = -4,        /* a leading dimension is too small or not a multiple of 8 */
+    MQ_ERR_LD = -4,        /* a leading dimension is too small, too large or not a
+                              multiple of 8 (of 4 for f32 activation rows) */
     MQ_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
     MQ_ERR_WORKSPACE = -6, /* workspace missing or smaller than mq_gemm_workspace_bytes */
     MQ_ERR_SPLIT = -7,     /* split_k outside 0..MQ_MAX_SPLIT_K */
@@ -184,6 +185,46 @@ int mq_gemm_f16cache(const uint16_t *X, int ldx, const uint16_t *W16, int ldw, f
  * the same product of the same operands. */
 int mq_gemm_fused(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y, int ldy,
                   int M, int N, int K, void *ws, size_t ws_bytes, int split_k, void *stream);
+
+/* f32 activations.  Fucina "Eager GPU Offload Without A Compute Graph",
+ * quantized linears: the callers hold f32 activations, and the GEMM rounds
+ * them to f16 while it stages the operand tile instead of in a separate pass
+ * (llama.cpp PR #57, batch-size dependence: that separate convert is part of
+ * what the f16 path loses at small M).
+ *
+ * mq_gemm_f16cache_xf32 / mq_gemm_fused_xf32 compute Y[M×N] = X16·Wᵀ with
+ * X16 = f16_rne(X) (round to nearest even, subnormals kept, overflow to
+ * ±inf), to the accuracy contract of mq_gemm_f16cache.  Without a K split
+ * (split_k = 1) each output sums the same products in the same order as
+ * mq_gemm_f16cache / mq_gemm_fused on X16, so the two agree bit for bit; the
+ * automatic split may differ, since these kernels use other tiles.
+ *   X   : device f32, 16-byte aligned, row stride ldx (>= K, multiple of 4,
+ *         <= MQ_MAX_K).
+ *   ws  : ws_bytes >= mq_gemm_xf32_workspace_bytes(fmt, M, N, K, split_k)
+ *         (these kernels use other tiles than the f16-activation ones, so
+ *         their split planes differ).
+ *   other arguments and errors as mq_gemm_f16cache / mq_gemm_fused. */
+int64_t mq_gemm_xf32_workspace_bytes(int fmt, int M, int N, int K, int split_k);
+
+int mq_gemm_f16cache_xf32(const float *X, int ldx, const uint16_t *W16, int ldw, float *Y,
+                          int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
+                          void *stream);
+
+int mq_gemm_fused_xf32(int fmt, const float *X, int ldx, const void *wq, float *Y, int ldy,
+                       int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
+                       void *stream);
+
+/* The standalone activation convert: X16[m·ld16 + k] = f16_rne(X[m·ldx + k])
+ * for m < M, k < K; columns >= K of X16 are not written.  For callers that
+ * share one converted X between several GEMMs (one pass instead of one per
+ * GEMM).  HBM-bound: 6 bytes per element.
+ *   X   : device f32, 16-byte aligned, row stride ldx (>= K, multiple of 4,
+ *         <= MQ_MAX_K).
+ *   X16 : device f16, 16-byte aligned, row stride ld16 (>= K, multiple of 8).
+ *   K   : multiple of 8.
+ * Errors: MQ_ERR_NULL, MQ_ERR_SHAPE, MQ_ERR_LD, MQ_ERR_ALIGN, MQ_ERR_HIP. */
+int mq_convert_f32_to_f16(const float *X, int ldx, uint16_t *X16, int ld16, int M, int K,
+                          void *stream);
 
 /* Static text for a return code (never NULL). */
 const char *mq_strerror(int code);

@@ -19,6 +19,10 @@ What it computes (sources are the four pages the method is described on):
   Summary, second bullet).
 * ``gemm_ref`` — Y = X·Wᵀ over the f16 operands, evaluated exactly in f64,
   plus S = |X|·|W|ᵀ for the per-element tolerance 1e-3·S + 1e-5.
+* ``activations_to_f16`` — f32 activations rounded once to f16 (Fucina "Eager
+  GPU Offload Without A Compute Graph", quantized linears: f32 activations
+  converted to half as the operand tile is staged); the f32-activation GEMM
+  is ``gemm_ref`` on that.
 
 Every function is pinned by ``-m "not gpu"`` tests against hand-derived
 worked vectors, closed forms, an independent field-wise encoder, exact
@@ -43,9 +47,12 @@ from .formats import (
     q4k_scale_min,
     row_bytes,
 )
-from .gemm import gemm_ref, gemm_bruteforce, within_tolerance
+from .gemm import (activations_to_f16, activations_to_f16_scalar, gemm_bruteforce, gemm_ref,
+                   within_tolerance)
 
 __all__ = [
+    "activations_to_f16",
+    "activations_to_f16_scalar",
     "BLOCK_BYTES",
     "BLOCK_ELEMS",
     "Q4_0",

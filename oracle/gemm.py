@@ -22,6 +22,33 @@ import math
 import numpy as np
 
 
+def activations_to_f16(x: np.ndarray) -> np.ndarray:
+    """f16 bit patterns of f32 activations, each rounded once to the nearest
+    binary16 (ties to even, subnormals kept, overflow to ±inf).
+
+    The pages' callers hold f32 activations; the f16 GEMM consumes them
+    converted to half (Fucina "Eager GPU Offload Without A Compute Graph",
+    quantized linears: f32 activation loads converted with half2 conversions
+    into the half operand tile; llama.cpp PR #57, batch-size dependence: the
+    activation convert ahead of the f16 GEMM).  The f32-activation GEMM is
+    therefore ``gemm_ref(activations_to_f16(x), w)``.  numpy's float32 →
+    float16 cast is that single rounding.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):        # overflow to ±inf is the defined result
+        return x.astype(np.float16).view(np.uint16)
+
+
+def activations_to_f16_scalar(x: np.ndarray) -> np.ndarray:
+    """The same rounding element by element with the IEEE converter of
+    ``oracle.f16`` (small inputs only); a second, independent implementation."""
+    from .f16 import f32_to_f16_bits
+
+    x = np.asarray(x, dtype=np.float32)
+    flat = [f32_to_f16_bits(float(v)) for v in x.reshape(-1)]
+    return np.array(flat, dtype=np.uint16).reshape(x.shape)
+
+
 def _as_f64(bits: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 

@@ -23,6 +23,7 @@ from .api import (
     block_bytes,
     block_elems,
     cache_ld,
+    convert_f32_to_f16,
     dequant_to_f16,
     dequant_to_f16_batch,
     gemm_f16cache,
@@ -45,6 +46,7 @@ __all__ = [
     "block_bytes",
     "block_elems",
     "cache_ld",
+    "convert_f32_to_f16",
     "dequant_to_f16",
     "dequant_to_f16_batch",
     "gemm_f16cache",

@@ -58,9 +58,12 @@ def cache_ld(K: int) -> int:
     return check(lib().mq_f16cache_ld(K), "mq_f16cache_ld")
 
 
-def workspace_bytes(fmt, M: int, N: int, K: int, split_k: int = 0) -> int:
+def workspace_bytes(fmt, M: int, N: int, K: int, split_k: int = 0, x_f32: bool = False) -> int:
+    """Workspace bytes of a GEMM (fmt 0 / "f16": the f16 cache); x_f32 for f32
+    activations."""
     f = 0 if fmt in (0, None, "f16") else _fmt(fmt)
-    return check(lib().mq_gemm_workspace_bytes(f, M, N, K, split_k), "mq_gemm_workspace_bytes")
+    fn = "mq_gemm_xf32_workspace_bytes" if x_f32 else "mq_gemm_workspace_bytes"
+    return check(getattr(lib(), fn)(f, M, N, K, split_k), fn)
 
 
 def dequant_to_f16(wq: torch.Tensor, fmt, N: int, K: int, pad: bool = True,
@@ -110,18 +113,28 @@ def dequant_to_f16_batch(jobs, pad: bool = True) -> list[torch.Tensor]:
     return outs
 
 
-def _workspace(fmt_code: int, M: int, N: int, K: int, split_k: int, device) -> torch.Tensor | None:
-    nbytes = check(lib().mq_gemm_workspace_bytes(fmt_code, M, N, K, split_k),
-                   "mq_gemm_workspace_bytes")
+def _workspace(fmt_code: int, M: int, N: int, K: int, split_k: int, device,
+               x_f32: bool = False) -> torch.Tensor | None:
+    nbytes = workspace_bytes(fmt_code, M, N, K, split_k, x_f32)
     if nbytes == 0:
         return None
     return torch.empty(nbytes // 4, dtype=torch.float32, device=device)
 
 
+def _x_kind(x: torch.Tensor) -> bool:
+    """True for f32 activations (the _xf32 entry points), False for f16."""
+    if x.dtype == torch.float32:
+        _need_cuda(x, "x", torch.float32)
+        return True
+    _need_cuda(x, "x", torch.float16)
+    return False
+
+
 def gemm_f16cache(x: torch.Tensor, w16: torch.Tensor, K: int | None = None, split_k: int = 0,
                   out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
-    """Y[M, N] (f32) = x[:, :K] @ w16[:, :K]^T with x f16 [M, >=K], w16 the f16 cache [N, ld]."""
-    _need_cuda(x, "x", torch.float16)
+    """Y[M, N] (f32) = x[:, :K] @ w16[:, :K]^T with x [M, >=K] (f16, or f32
+    rounded to f16 inside the kernel), w16 the f16 cache [N, ld]."""
+    xf32 = _x_kind(x)
     _need_cuda(w16, "w16", torch.float16)
     ldx = _row_major_2d(x, "x")
     ldw = _row_major_2d(w16, "w16")
@@ -133,21 +146,22 @@ def gemm_f16cache(x: torch.Tensor, w16: torch.Tensor, K: int | None = None, spli
         _need_cuda(out, "out", torch.float32)
     ldy = _row_major_2d(out, "out")
     if ws is None:
-        ws = _workspace(0, M, N, K, split_k, x.device)
-    check(lib().mq_gemm_f16cache(x.data_ptr(), ldx, w16.data_ptr(), ldw, out.data_ptr(), ldy,
-                                 M, N, K, 0 if ws is None else ws.data_ptr(),
-                                 0 if ws is None else ws.numel() * ws.element_size(),
-                                 split_k, _stream(x)),
-          "mq_gemm_f16cache")
+        ws = _workspace(0, M, N, K, split_k, x.device, xf32)
+    fn = "mq_gemm_f16cache_xf32" if xf32 else "mq_gemm_f16cache"
+    check(getattr(lib(), fn)(x.data_ptr(), ldx, w16.data_ptr(), ldw, out.data_ptr(), ldy,
+                             M, N, K, 0 if ws is None else ws.data_ptr(),
+                             0 if ws is None else ws.numel() * ws.element_size(),
+                             split_k, _stream(x)), fn)
     return out
 
 
 def gemm_fused(x: torch.Tensor, wq: torch.Tensor, fmt, N: int, K: int | None = None,
                split_k: int = 0, out: torch.Tensor | None = None,
                ws: torch.Tensor | None = None) -> torch.Tensor:
-    """Y[M, N] (f32) = x[:, :K] @ dequant(wq)^T, expanding the quantized weight in-kernel."""
+    """Y[M, N] (f32) = x[:, :K] @ dequant(wq)^T, expanding the quantized weight
+    in-kernel; x f16, or f32 rounded to f16 inside the kernel."""
     f = _fmt(fmt)
-    _need_cuda(x, "x", torch.float16)
+    xf32 = _x_kind(x)
     _need_cuda(wq, "wq", torch.uint8)
     if not wq.is_contiguous():
         raise ValueError("wq must be contiguous")
@@ -160,10 +174,27 @@ def gemm_fused(x: torch.Tensor, wq: torch.Tensor, fmt, N: int, K: int | None = N
         _need_cuda(out, "out", torch.float32)
     ldy = _row_major_2d(out, "out")
     if ws is None:
-        ws = _workspace(f, M, N, K, split_k, x.device)
-    check(lib().mq_gemm_fused(f, x.data_ptr(), ldx, wq.data_ptr(), out.data_ptr(), ldy, M, N, K,
-                              0 if ws is None else ws.data_ptr(),
-                              0 if ws is None else ws.numel() * ws.element_size(),
-                              split_k, _stream(x)),
-          "mq_gemm_fused")
+        ws = _workspace(f, M, N, K, split_k, x.device, xf32)
+    fn = "mq_gemm_fused_xf32" if xf32 else "mq_gemm_fused"
+    check(getattr(lib(), fn)(f, x.data_ptr(), ldx, wq.data_ptr(), out.data_ptr(), ldy, M, N, K,
+                             0 if ws is None else ws.data_ptr(),
+                             0 if ws is None else ws.numel() * ws.element_size(),
+                             split_k, _stream(x)), fn)
+    return out
+
+
+def convert_f32_to_f16(x: torch.Tensor, K: int | None = None,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """f16 copy (round to nearest even) of the f32 activations x[:, :K]."""
+    _need_cuda(x, "x", torch.float32)
+    ldx = _row_major_2d(x, "x")
+    M = x.shape[0]
+    K = x.shape[1] if K is None else K
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float16, device=x.device)
+    else:
+        _need_cuda(out, "out", torch.float16)
+    ld16 = _row_major_2d(out, "out")
+    check(lib().mq_convert_f32_to_f16(x.data_ptr(), ldx, out.data_ptr(), ld16, M, K, _stream(x)),
+          "mq_convert_f32_to_f16")
     return out

@@ -25,6 +25,10 @@ int check_dims(int M, int N, int K) {
 
 bool ld_ok(int64_t ld, int64_t K) { return ld >= K && ld % 8 == 0 && ld <= MQ_MAX_K + 64; }
 
+// f32 activation rows: 16-byte aligned (ld a multiple of 4), at most MQ_MAX_K
+// elements apart (a 256-row tile then spans at most 2^31 bytes).
+bool ld32_ok(int64_t ld, int64_t K) { return ld >= K && ld % 4 == 0 && ld <= MQ_MAX_K; }
+
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return MQ_OK;
     g_last_hip_error = (int)e;
@@ -45,18 +49,18 @@ int check_dequant(int fmt, const void *wq, int N, int K, const uint16_t *w16, in
 // Shared checks of both GEMM entry points; fills the plan on success.
 int check_gemm(int fmt, const void *X, int ldx, const void *W, int64_t ldw_elems, const float *Y,
                int ldy, int M, int N, int K, const void *ws, size_t ws_bytes, int split_k,
-               mq::GemmPlan *plan) {
+               mq::GemmPlan *plan, bool x_f32 = false) {
     if (!X || !W || !Y) return MQ_ERR_NULL;
     if (fmt != mq::kFmtF16 && !quant_fmt(fmt)) return MQ_ERR_FORMAT;
     if (int rc = check_dims(M, N, K)) return rc;
     const int step = fmt == mq::kFmtF16 ? 8 : mq::block_elems(fmt);
     if (K % step) return MQ_ERR_SHAPE;
-    if (!ld_ok(ldx, K) || ldy < N) return MQ_ERR_LD;
+    if (!(x_f32 ? ld32_ok(ldx, K) : ld_ok(ldx, K)) || ldy < N) return MQ_ERR_LD;
     if (fmt == mq::kFmtF16 && !ld_ok(ldw_elems, K)) return MQ_ERR_LD;
     if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return MQ_ERR_ALIGN;
     if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
     if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
-    *plan = mq::plan_gemm(fmt, M, N, K, split_k);
+    *plan = mq::plan_gemm(fmt, M, N, K, split_k, x_f32);
     if (plan->ws_bytes > 0 &&
         (!ws || !aligned16(ws) || ws_bytes < (size_t)plan->ws_bytes))
         return MQ_ERR_WORKSPACE;
@@ -116,13 +120,21 @@ int mq_dequant_to_f16_batch(const mq_dequant_job *jobs, int n, void *stream) {
     return MQ_OK;
 }
 
-int64_t mq_gemm_workspace_bytes(int fmt, int M, int N, int K, int split_k) {
+static int64_t workspace_bytes(int fmt, int M, int N, int K, int split_k, bool x_f32) {
     if (fmt != mq::kFmtF16 && !quant_fmt(fmt)) return MQ_ERR_FORMAT;
     if (int rc = check_dims(M, N, K)) return rc;
     if (K % (fmt == mq::kFmtF16 ? 8 : mq::block_elems(fmt))) return MQ_ERR_SHAPE;
     if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
     if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
-    return mq::plan_gemm(fmt, M, N, K, split_k).ws_bytes;
+    return mq::plan_gemm(fmt, M, N, K, split_k, x_f32).ws_bytes;
+}
+
+int64_t mq_gemm_workspace_bytes(int fmt, int M, int N, int K, int split_k) {
+    return workspace_bytes(fmt, M, N, K, split_k, false);
+}
+
+int64_t mq_gemm_xf32_workspace_bytes(int fmt, int M, int N, int K, int split_k) {
+    return workspace_bytes(fmt, M, N, K, split_k, true);
 }
 
 int mq_gemm_f16cache(const uint16_t *X, int ldx, const uint16_t *W16, int ldw, float *Y,
@@ -147,13 +159,46 @@ int mq_gemm_fused(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y,
                                       (float *)ws, (hipStream_t)stream));
 }
 
+int mq_gemm_f16cache_xf32(const float *X, int ldx, const uint16_t *W16, int ldw, float *Y,
+                          int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
+                          void *stream) {
+    mq::GemmPlan plan;
+    if (int rc = check_gemm(mq::kFmtF16, X, ldx, W16, ldw, Y, ldy, M, N, K, ws, ws_bytes,
+                            split_k, &plan, true))
+        return rc;
+    return hip_status(mq::launch_gemm_xf32(mq::kFmtF16, X, ldx, W16, ldw, Y, ldy, M, N, K, plan,
+                                           (float *)ws, (hipStream_t)stream));
+}
+
+int mq_gemm_fused_xf32(int fmt, const float *X, int ldx, const void *wq, float *Y, int ldy,
+                       int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
+                       void *stream) {
+    if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    mq::GemmPlan plan;
+    if (int rc = check_gemm(fmt, X, ldx, wq, 0, Y, ldy, M, N, K, ws, ws_bytes, split_k, &plan,
+                            true))
+        return rc;
+    const int64_t row_bytes = (int64_t)K / mq::block_elems(fmt) * mq::block_bytes(fmt);
+    return hip_status(mq::launch_gemm_xf32(fmt, X, ldx, wq, row_bytes, Y, ldy, M, N, K, plan,
+                                           (float *)ws, (hipStream_t)stream));
+}
+
+int mq_convert_f32_to_f16(const float *X, int ldx, uint16_t *X16, int ld16, int M, int K,
+                          void *stream) {
+    if (!X || !X16) return MQ_ERR_NULL;
+    if (check_dims(M, 1, K) || K % 8) return MQ_ERR_SHAPE;
+    if (!ld32_ok(ldx, K) || !ld_ok(ld16, K)) return MQ_ERR_LD;
+    if (!aligned16(X) || !aligned16(X16)) return MQ_ERR_ALIGN;
+    return hip_status(mq::launch_convert_f32_to_f16(X, ldx, X16, ld16, M, K, (hipStream_t)stream));
+}
+
 const char *mq_strerror(int code) {
     switch (code) {
     case MQ_OK: return "success";
     case MQ_ERR_NULL: return "a required pointer is NULL";
     case MQ_ERR_FORMAT: return "unknown weight format";
     case MQ_ERR_SHAPE: return "M, N or K out of range, or K not a multiple of the block size";
-    case MQ_ERR_LD: return "a leading dimension is too small, too large or not a multiple of 8";
+    case MQ_ERR_LD: return "a leading dimension is too small, too large or not a multiple of 8 (4 for f32 rows)";
     case MQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MQ_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than required";
     case MQ_ERR_SPLIT: return "split_k out of range for this problem";

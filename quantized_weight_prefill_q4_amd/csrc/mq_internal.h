@@ -64,7 +64,8 @@ struct GemmPlan {
 };
 
 // split_req: 0 = choose, 1..16 = requested partitions (clamped to the k-steps).
-GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req);
+// x_f32: the activations are f32 (converted to f16 in the A-tile load).
+GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32 = false);
 
 // Launch the GEMM (and the split-K reduction when plan.split > 1).
 //   W    : uint16 f16 cache when fmt == kFmtF16, else quantized bytes.
@@ -72,5 +73,15 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req);
 hipError_t launch_gemm(int fmt, const uint16_t *X, int ldx, const void *W, int64_t ldw,
                        float *Y, int ldy, int M, int N, int K, const GemmPlan &plan, float *ws,
                        hipStream_t stream);
+
+// The same GEMM with f32 activations X (row stride ldx in elements), each
+// rounded to f16 as its tile is staged; plan from plan_gemm(..., true).
+hipError_t launch_gemm_xf32(int fmt, const float *X, int ldx, const void *W, int64_t ldw,
+                            float *Y, int ldy, int M, int N, int K, const GemmPlan &plan,
+                            float *ws, hipStream_t stream);
+
+// X16[m·ld16 + k] = f16_rne(X[m·ldx + k]) for m < M, k < K (K a multiple of 8).
+hipError_t launch_convert_f32_to_f16(const float *X, int ldx, uint16_t *X16, int ld16, int M,
+                                     int K, hipStream_t stream);
 
 }  // namespace mq

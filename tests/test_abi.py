@@ -124,6 +124,38 @@ def test_fused_rejects(L):
     assert f(12, FAKE, 512, FAKE, FAKE, 256, 64, 256, 512, None, 0, 4, None) == _lib.MQ_ERR_WORKSPACE
 
 
+def test_xf32_entry_points_reject(L):
+    """f32 activations: rows 16-byte aligned (ldx a multiple of 4, not 8) and
+    at most MQ_MAX_K apart; the other checks as the f16 entry points."""
+    c = L.mq_gemm_f16cache_xf32
+    f = L.mq_gemm_fused_xf32
+    # (X, ldx, W16, ldw, Y, ldy, M, N, K, ws, wsb, split, stream) with one bad value each
+    assert c(FAKE, 514, FAKE, 512, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_LD
+    assert c(FAKE, 504, FAKE, 512, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_LD
+    assert c(FAKE, (1 << 21) + 4, FAKE, 512, FAKE, 256, 64, 256, 512, None, 0, 1,
+             None) == _lib.MQ_ERR_LD
+    assert c(None, 512, FAKE, 512, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_NULL
+    assert c(MIS, 512, FAKE, 512, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_ALIGN
+    assert c(FAKE, 512, FAKE, 512, FAKE, 256, 64, 256, 512, None, 0, 4, None) == _lib.MQ_ERR_WORKSPACE
+    assert f(5, FAKE, 512, FAKE, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_FORMAT
+    assert f(12, FAKE, 512, FAKE, FAKE, 256, 64, 256, 480, None, 0, 1, None) == _lib.MQ_ERR_SHAPE
+    assert f(12, FAKE, 510, FAKE, FAKE, 256, 64, 256, 256, None, 0, 1, None) == _lib.MQ_ERR_LD
+    assert f(12, FAKE, 512, FAKE, FAKE, 255, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_LD
+    assert f(13, FAKE, 512, FAKE, MIS, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_ALIGN
+    assert f(2, FAKE, 512, FAKE, FAKE, 256, 64, 256, 512, None, 0, 17, None) == _lib.MQ_ERR_SPLIT
+    v = L.mq_convert_f32_to_f16
+    # (X, ldx, X16, ld16, M, K, stream)
+    assert v(None, 512, FAKE, 512, 4, 512, None) == _lib.MQ_ERR_NULL
+    assert v(FAKE, 512, None, 512, 4, 512, None) == _lib.MQ_ERR_NULL
+    assert v(FAKE, 512, FAKE, 512, 0, 512, None) == _lib.MQ_ERR_SHAPE
+    assert v(FAKE, 512, FAKE, 512, 4, 12, None) == _lib.MQ_ERR_SHAPE
+    assert v(FAKE, 510, FAKE, 512, 4, 504, None) == _lib.MQ_ERR_LD
+    assert v(FAKE, 512, FAKE, 508, 4, 504, None) == _lib.MQ_ERR_LD
+    assert v(FAKE, 512, FAKE, 500, 4, 504, None) == _lib.MQ_ERR_LD
+    assert v(MIS, 512, FAKE, 512, 4, 512, None) == _lib.MQ_ERR_ALIGN
+    assert v(FAKE, 512, MIS, 512, 4, 512, None) == _lib.MQ_ERR_ALIGN
+
+
 def test_dequant_batch_rejects(L):
     J = _lib.MqDequantJob
     ok = J(12, 64, 256, 256, FAKE, FAKE)
@@ -164,6 +196,13 @@ def test_workspace_planning(L):
     # forced splits are clamped to the number of 64-wide k-steps
     assert L.mq_gemm_workspace_bytes(0, 64, 128, 128, 16) == 2 * 64 * 128 * 4
     assert L.mq_gemm_workspace_bytes(99, 64, 128, 128, 1) == _lib.MQ_ERR_FORMAT
+    # f32 activations never take the 256 x 256 tile: gate/up on 256 x 128 tiles
+    # is 4 rounds + 160 tiles, not split; k/v still splits as the f16 plan does
+    for fmt in (0, 2, 12, 13, 14):
+        assert L.mq_gemm_xf32_workspace_bytes(fmt, 2048, 18944, 3584, 0) == 0
+    assert L.mq_gemm_xf32_workspace_bytes(12, 2048, 512, 3584, 0) == ws
+    assert L.mq_gemm_xf32_workspace_bytes(0, 64, 128, 128, 16) == 2 * 64 * 128 * 4
+    assert L.mq_gemm_xf32_workspace_bytes(99, 64, 128, 128, 1) == _lib.MQ_ERR_FORMAT
 
 
 def test_strerror_total(L):
