@@ -335,10 +335,11 @@ def formats_table(torch, mq, dev, log_rows):
 
 def xf32_table(torch, mq, dev, log_rows):
     """f32 activations on the Llama-3.1-8B gate/up shape (N = 14336, K = 4096),
-    for the f16 cache and the fused Q4_K GEMM: the f32-activation kernel
-    (rounds X to f16 while staging its tile) against the standalone convert
-    followed by the f16-activation kernel, per M; the f16-activation kernel
-    alone for reference.  Weight copies rotate over > 512 MB."""
+    for the f16 cache and the fused Q4_K GEMM, per M: the f32-activation entry
+    point (in-tile rounding up to M = 64, else one convert pass into the
+    workspace and the f16 kernel), against the caller converting X itself and
+    calling the f16-activation entry point; that entry point alone for
+    reference.  Weight copies rotate over > 512 MB."""
     N, K = 14336, 4096
     fmt = mq.FORMATS["q4_k"]
     q0 = synth.weights_device(fmt, 6300, N, K, dev)
@@ -352,7 +353,7 @@ def xf32_table(torch, mq, dev, log_rows):
     x32 = torch.randn((2048, K), generator=g, device=dev, dtype=torch.float32)
     x16 = torch.empty((2048, K), dtype=torch.float16, device=dev)
     out = {}
-    for M in (128, 512, 2048):
+    for M in (64, 128, 512, 2048):
         xm32, xm16 = x32[:M], x16[:M]
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         rec = {"convert_us": round(_median_us(torch, lambda r: mq.convert_f32_to_f16(xm32, out=xm16), 12), 2)}
@@ -374,11 +375,13 @@ def xf32_table(torch, mq, dev, log_rows):
             rec[path] = {"x16_us": round(t16, 2), "xf32_us": round(t32, 2),
                          "convert_then_x16_us": round(tcv, 2),
                          "xf32_tflops": round(2.0 * M * N * K / t32 / 1e6, 1)}
-            log_rows.append(f"  {path:5s} M={M:5d}  f16 X {t16:8.1f} us   f32 X in-kernel {t32:8.1f} us"
-                            f"   convert + f16 X {tcv:8.1f} us   (convert alone {rec['convert_us']:.1f} us)")
+            how = "in-tile" if M <= 64 else "convert-first"
+            log_rows.append(f"  {path:5s} M={M:5d}  f16 X {t16:8.1f} us   f32 X ({how}) {t32:8.1f} us"
+                            f"   caller convert + f16 X {tcv:8.1f} us   (convert alone {rec['convert_us']:.1f} us)")
         out[M] = rec
+    ms = sorted(out)
     for path in ("cache", "fused"):
-        wins = [M for M in sorted(out) if out[M][path]["convert_then_x16_us"] < out[M][path]["xf32_us"]]
+        wins = [M for M in ms if out[M][path]["convert_then_x16_us"] < out[M][path]["xf32_us"]]
         out[f"{path}_convert_first_from_M"] = wins[0] if wins else None
     del qs, caches, x32, x16
     torch.cuda.empty_cache()

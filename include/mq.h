@@ -200,10 +200,17 @@ int mq_gemm_fused(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y,
  * automatic split may differ, since these kernels use other tiles.
  *   X   : device f32, 16-byte aligned, row stride ldx (>= K, multiple of 4,
  *         <= MQ_MAX_K).
- *   ws  : ws_bytes >= mq_gemm_xf32_workspace_bytes(fmt, M, N, K, split_k)
- *         (these kernels use other tiles than the f16-activation ones, so
- *         their split planes differ).
- *   other arguments and errors as mq_gemm_f16cache / mq_gemm_fused. */
+ *   ws  : ws_bytes >= mq_gemm_xf32_workspace_bytes(fmt, M, N, K, split_k).
+ *   other arguments and errors as mq_gemm_f16cache / mq_gemm_fused.
+ * Two ways to run, chosen by M (the result is the same):
+ *   M <= 64: the kernel rounds X to f16 as it stages each A tile (no extra
+ *            pass; the workspace holds only K-split planes);
+ *   M >  64: X is rounded once into the front of the workspace (M rows of
+ *            mq_f16cache_ld(K) halves, rounded up to 256 bytes), then the
+ *            f16-activation kernel runs on it.  Every column tile of the
+ *            output re-reads the A panel, so in-tile conversion repeats the
+ *            rounding N/BN times and doubles the A bytes through the compute
+ *            units; one 6-byte-per-element pass is cheaper here. */
 int64_t mq_gemm_xf32_workspace_bytes(int fmt, int M, int N, int K, int split_k);
 
 int mq_gemm_f16cache_xf32(const float *X, int ldx, const uint16_t *W16, int ldw, float *Y,

@@ -46,10 +46,40 @@ int check_dequant(int fmt, const void *wq, int N, int K, const uint16_t *w16, in
     return MQ_OK;
 }
 
+// How a GEMM with f32 activations runs.  Up to kInTileMaxM rows the kernel
+// rounds X to f16 while staging its tiles; above, X is converted once into
+// the front of the workspace and the f16-activation kernel (with its own
+// plan, 256 × 256 tiles included) reads it: every column tile re-reads the
+// X panel, so converting inside the tile costs N/BN conversions and twice
+// the A-operand bytes per element, against one 6-byte pass.
+constexpr int kInTileMaxM = 64;
+
+struct XPlan {
+    bool convert_first;
+    int ld16;               // row stride of the converted X (convert_first)
+    int64_t x16_bytes;      // its workspace bytes, a multiple of 256 (else 0)
+    mq::GemmPlan gemm;      // split planes follow the converted X in the workspace
+};
+
+XPlan xf32_plan(int fmt, int M, int N, int K, int split_k) {
+    XPlan xp;
+    xp.convert_first = M > kInTileMaxM;
+    if (xp.convert_first) {
+        xp.ld16 = (int)mq_f16cache_ld(K);
+        xp.x16_bytes = ((int64_t)M * xp.ld16 * 2 + 255) / 256 * 256;
+        xp.gemm = mq::plan_gemm(fmt, M, N, K, split_k, false);
+    } else {
+        xp.ld16 = 0;
+        xp.x16_bytes = 0;
+        xp.gemm = mq::plan_gemm(fmt, M, N, K, split_k, true);
+    }
+    return xp;
+}
+
 // Shared checks of both GEMM entry points; fills the plan on success.
 int check_gemm(int fmt, const void *X, int ldx, const void *W, int64_t ldw_elems, const float *Y,
                int ldy, int M, int N, int K, const void *ws, size_t ws_bytes, int split_k,
-               mq::GemmPlan *plan, bool x_f32 = false) {
+               mq::GemmPlan *plan, bool x_f32 = false, XPlan *xplan = nullptr) {
     if (!X || !W || !Y) return MQ_ERR_NULL;
     if (fmt != mq::kFmtF16 && !quant_fmt(fmt)) return MQ_ERR_FORMAT;
     if (int rc = check_dims(M, N, K)) return rc;
@@ -60,11 +90,31 @@ int check_gemm(int fmt, const void *X, int ldx, const void *W, int64_t ldw_elems
     if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return MQ_ERR_ALIGN;
     if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
     if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
-    *plan = mq::plan_gemm(fmt, M, N, K, split_k, x_f32);
-    if (plan->ws_bytes > 0 &&
-        (!ws || !aligned16(ws) || ws_bytes < (size_t)plan->ws_bytes))
-        return MQ_ERR_WORKSPACE;
+    int64_t need;
+    if (x_f32) {
+        *xplan = xf32_plan(fmt, M, N, K, split_k);
+        *plan = xplan->gemm;
+        need = xplan->x16_bytes + plan->ws_bytes;
+    } else {
+        *plan = mq::plan_gemm(fmt, M, N, K, split_k);
+        need = plan->ws_bytes;
+    }
+    if (need > 0 && (!ws || !aligned16(ws) || ws_bytes < (size_t)need)) return MQ_ERR_WORKSPACE;
     return MQ_OK;
+}
+
+// The f32-activation GEMM: in-tile conversion, or convert into the
+// workspace and the f16-activation kernel.
+int run_xf32(int fmt, const float *X, int ldx, const void *W, int64_t ldw, float *Y, int ldy,
+             int M, int N, int K, void *ws, const XPlan &xp, hipStream_t stream) {
+    if (!xp.convert_first)
+        return hip_status(mq::launch_gemm_xf32(fmt, X, ldx, W, ldw, Y, ldy, M, N, K, xp.gemm,
+                                               (float *)ws, stream));
+    uint16_t *x16 = (uint16_t *)ws;
+    if (int rc = hip_status(mq::launch_convert_f32_to_f16(X, ldx, x16, xp.ld16, M, K, stream)))
+        return rc;
+    return hip_status(mq::launch_gemm(fmt, x16, xp.ld16, W, ldw, Y, ldy, M, N, K, xp.gemm,
+                                      (float *)((char *)ws + xp.x16_bytes), stream));
 }
 
 }  // namespace
@@ -126,7 +176,9 @@ static int64_t workspace_bytes(int fmt, int M, int N, int K, int split_k, bool x
     if (K % (fmt == mq::kFmtF16 ? 8 : mq::block_elems(fmt))) return MQ_ERR_SHAPE;
     if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
     if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
-    return mq::plan_gemm(fmt, M, N, K, split_k, x_f32).ws_bytes;
+    if (!x_f32) return mq::plan_gemm(fmt, M, N, K, split_k).ws_bytes;
+    const XPlan xp = xf32_plan(fmt, M, N, K, split_k);
+    return xp.x16_bytes + xp.gemm.ws_bytes;
 }
 
 int64_t mq_gemm_workspace_bytes(int fmt, int M, int N, int K, int split_k) {
@@ -163,11 +215,11 @@ int mq_gemm_f16cache_xf32(const float *X, int ldx, const uint16_t *W16, int ldw,
                           int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
                           void *stream) {
     mq::GemmPlan plan;
+    XPlan xp;
     if (int rc = check_gemm(mq::kFmtF16, X, ldx, W16, ldw, Y, ldy, M, N, K, ws, ws_bytes,
-                            split_k, &plan, true))
+                            split_k, &plan, true, &xp))
         return rc;
-    return hip_status(mq::launch_gemm_xf32(mq::kFmtF16, X, ldx, W16, ldw, Y, ldy, M, N, K, plan,
-                                           (float *)ws, (hipStream_t)stream));
+    return run_xf32(mq::kFmtF16, X, ldx, W16, ldw, Y, ldy, M, N, K, ws, xp, (hipStream_t)stream);
 }
 
 int mq_gemm_fused_xf32(int fmt, const float *X, int ldx, const void *wq, float *Y, int ldy,
@@ -175,12 +227,12 @@ int mq_gemm_fused_xf32(int fmt, const float *X, int ldx, const void *wq, float *
                        void *stream) {
     if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
     mq::GemmPlan plan;
+    XPlan xp;
     if (int rc = check_gemm(fmt, X, ldx, wq, 0, Y, ldy, M, N, K, ws, ws_bytes, split_k, &plan,
-                            true))
+                            true, &xp))
         return rc;
     const int64_t row_bytes = (int64_t)K / mq::block_elems(fmt) * mq::block_bytes(fmt);
-    return hip_status(mq::launch_gemm_xf32(fmt, X, ldx, wq, row_bytes, Y, ldy, M, N, K, plan,
-                                           (float *)ws, (hipStream_t)stream));
+    return run_xf32(fmt, X, ldx, wq, row_bytes, Y, ldy, M, N, K, ws, xp, (hipStream_t)stream);
 }
 
 int mq_convert_f32_to_f16(const float *X, int ldx, uint16_t *X16, int ld16, int M, int K,

@@ -196,12 +196,20 @@ def test_workspace_planning(L):
     # forced splits are clamped to the number of 64-wide k-steps
     assert L.mq_gemm_workspace_bytes(0, 64, 128, 128, 16) == 2 * 64 * 128 * 4
     assert L.mq_gemm_workspace_bytes(99, 64, 128, 128, 1) == _lib.MQ_ERR_FORMAT
-    # f32 activations never take the 256 x 256 tile: gate/up on 256 x 128 tiles
-    # is 4 rounds + 160 tiles, not split; k/v still splits as the f16 plan does
-    for fmt in (0, 2, 12, 13, 14):
-        assert L.mq_gemm_xf32_workspace_bytes(fmt, 2048, 18944, 3584, 0) == 0
-    assert L.mq_gemm_xf32_workspace_bytes(12, 2048, 512, 3584, 0) == ws
+    # f32 activations, M > 64: X rounded once into the front of the workspace
+    # (2048 rows of 3584 halves, already a multiple of 256 bytes), then the
+    # f16-activation plan with its split planes behind it
+    x16 = 2048 * 3584 * 2
+    for fmt in (0, 2, 12, 13):
+        assert L.mq_gemm_xf32_workspace_bytes(fmt, 2048, 18944, 3584, 0) == x16 + 3 * 80 * 256 * 256 * 4
+    assert L.mq_gemm_xf32_workspace_bytes(14, 2048, 18944, 3584, 0) == x16
+    assert L.mq_gemm_xf32_workspace_bytes(12, 2048, 512, 3584, 0) == x16 + ws
+    # padded row stride for the converted X when 2K bytes is a multiple of 2048;
+    # 65 rows of 4160 halves = 540800 bytes, rounded up to 540928
+    assert L.mq_gemm_xf32_workspace_bytes(0, 65, 4096, 4096, 1) == 540928
+    # M <= 64: in-tile conversion, own tiles (64 x 128), split planes only
     assert L.mq_gemm_xf32_workspace_bytes(0, 64, 128, 128, 16) == 2 * 64 * 128 * 4
+    assert L.mq_gemm_xf32_workspace_bytes(12, 64, 4096, 4096, 1) == 0
     assert L.mq_gemm_xf32_workspace_bytes(99, 64, 128, 128, 1) == _lib.MQ_ERR_FORMAT
 
 

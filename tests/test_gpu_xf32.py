@@ -2,10 +2,12 @@
 convert (bit for bit against ``oracle.activations_to_f16``) and both GEMM
 shapes with f32 X, whose defined result is the f16 GEMM on f16_rne(X):
 
+* both ways the library runs them: M <= 64 rounds X inside the A-tile load
+  (its own tiles), M > 64 converts X into the workspace first (padded row
+  stride when 2K bytes is a multiple of 2048) and runs the f16 kernel;
 * without a K split, bit-identical to the f16-activation entry point fed the
   oracle's rounding of X (so a conversion that rounds differently anywhere, or
-  a wrong stride, fails), at ragged shapes, padded f32 rows and the 256-row
-  tiles (which for f32 X are 256 × 128, against the f16 path's 256 × 256);
+  a wrong stride, fails), at ragged shapes and padded f32 rows;
 * integer-valued X and W exact, with automatic and forced K splits;
 * one-hot X reproduces the expanded weights for every format;
 * random inputs within the tolerance of the f64 oracle."""
@@ -85,9 +87,10 @@ def test_convert_beyond_one_grid():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("M,N,K,pad", [(1, 1, 8, 0), (7, 33, 56, 4), (65, 130, 72, 0),
-                                       (129, 257, 520, 8), (300, 1000, 1024, 4),
-                                       (2048, 8448, 2048, 0)])
+@pytest.mark.parametrize("M,N,K,pad", [(1, 1, 8, 0), (7, 33, 56, 4), (64, 200, 264, 4),
+                                       (65, 130, 72, 0), (64, 300, 4096, 0),
+                                       (100, 300, 4096, 4), (129, 257, 520, 8),
+                                       (300, 1000, 1024, 4), (2048, 8448, 2048, 0)])
 def test_cache_xf32_equals_f16_path_at_split1(M, N, K, pad):
     x = _x32(80 + M, M, K)
     w = oracle.activations_to_f16(_x32(81 + N, N, K))      # any f16 weights
@@ -102,9 +105,10 @@ def test_cache_xf32_equals_f16_path_at_split1(M, N, K, pad):
                rows=rows)
 
 
+@pytest.mark.parametrize("M", [37, 129])
 @pytest.mark.parametrize("fmt", ALL)
-def test_fused_xf32_random_tolerance_and_identity(fmt):
-    M, N, K = 129, 300, 1024 if fmt not in (12, 13, 14) else 1280
+def test_fused_xf32_random_tolerance_and_identity(fmt, M):
+    N, K = 300, 1024 if fmt not in (12, 13, 14) else 1280
     q = synth.weights(fmt, synth.rng(82, 0, fmt, 0), N, K)
     x = _x32(83, M, K)
     xd = _dev_x32(x, pad=4)
@@ -122,13 +126,19 @@ def test_fused_xf32_random_tolerance_and_identity(fmt):
 def test_fused_xf32_onehot_expansion(fmt):
     N, K = 130, 256
     q = synth.weights(fmt, synth.rng(84, 0, fmt, 0), N, K)
+    exp = oracle.dequant_ref(fmt, q, N, K).view(np.float16).astype(np.float32).T
     announce("gemm_fused_xf32", NAME[fmt], f"onehot K={K} N={N}")
     y = to_host(mq.gemm_fused(_dev_x32(_x32(0, K, K, "onehot")), to_dev_u8(q), fmt, N, K))
-    assert np.array_equal(y, oracle.dequant_ref(fmt, q, N, K).view(np.float16).astype(np.float32).T)
+    assert np.array_equal(y, exp)
+    # in-tile conversion: the first 64 rows of the identity give elements 0..63
+    announce("gemm_fused_xf32", NAME[fmt], f"onehot rows 0..63 K={K} N={N}")
+    y = to_host(mq.gemm_fused(_dev_x32(_x32(0, 64, K, "onehot")), to_dev_u8(q), fmt, N, K))
+    assert np.array_equal(y, exp[:64])
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [(12, 2048, 512, 3584), (14, 70, 130, 2048),
-                                       (8, 33, 257, 1056), (0, 100, 300, 1024),
+                                       (14, 50, 130, 2048), (8, 33, 257, 1056),
+                                       (0, 100, 300, 1024), (13, 64, 300, 2048),
                                        (13, 2048, 8448, 2048), (0, 2048, 8448, 2048)])
 @pytest.mark.parametrize("split", [0, 3])
 def test_xf32_integer_exact(fmt, M, N, K, split):
@@ -152,7 +162,6 @@ def test_xf32_integer_exact(fmt, M, N, K, split):
 
 
 def test_xf32_workspace_query_matches_binding():
-    for fmt, M, N, K in ((12, 2048, 512, 3584), (0, 2048, 18944, 3584), (14, 64, 4096, 4096)):
-        assert mq.workspace_bytes(fmt, M, N, K, 0, x_f32=True) >= 0
-    assert mq.workspace_bytes(12, 2048, 18944, 3584, 0, x_f32=True) == 0
-    assert mq.workspace_bytes(12, 2048, 18944, 3584, 0) > 0
+    assert mq.workspace_bytes(12, 2048, 18944, 3584, 0, x_f32=True) == \
+        2048 * 3584 * 2 + mq.workspace_bytes(12, 2048, 18944, 3584, 0)
+    assert mq.workspace_bytes(14, 64, 4096, 4096, 1, x_f32=True) == 0
