@@ -19,6 +19,10 @@ What it computes (sources are the four pages the method is described on):
   Summary, second bullet).
 * ``gemm_ref`` — Y = X·Wᵀ over the f16 operands, evaluated exactly in f64,
   plus S = |X|·|W|ᵀ for the per-element tolerance 1e-3·S + 1e-5.
+* ``mmq`` — the int8 product's own numerics (Fucina "Eager GPU Offload
+  Without A Compute Graph", the ik_llama.cpp audit: Q8_1-style activation
+  blocks, signed-int8 weights, int8 matrix instructions): ``quantize_q8_1``,
+  ``decompose`` (w = α·c − β per format), ``mmq_ref``.
 * ``activations_to_f16`` — f32 activations rounded once to f16 (Fucina "Eager
   GPU Offload Without A Compute Graph", quantized linears: f32 activations
   converted to half as the operand tile is staged); the f32-activation GEMM
@@ -47,10 +51,12 @@ from .formats import (
     q4k_scale_min,
     row_bytes,
 )
+from . import mmq
 from .gemm import (activations_to_f16, activations_to_f16_scalar, gemm_bruteforce, gemm_ref,
                    within_tolerance)
 
 __all__ = [
+    "mmq",
     "activations_to_f16",
     "activations_to_f16_scalar",
     "BLOCK_BYTES",
