@@ -233,6 +233,50 @@ int mq_gemm_fused_xf32(int fmt, const float *X, int ldx, const void *wq, float *
 int mq_convert_f32_to_f16(const float *X, int ldx, uint16_t *X16, int ld16, int M, int K,
                           void *stream);
 
+/* The int8 ("MMQ") product, a backend with numerics of its own (Fucina
+ * "Eager GPU Offload Without A Compute Graph", what the ik_llama.cpp audit
+ * contributed: f32 activations quantized once to a Q8_1-style int8 layout
+ * with scales and sums, weights unpacked to signed int8, int8 matrix
+ * instructions, under a separate parity gate).  Its result differs from the
+ * f16 paths' by the activation quantization; it reads the quantized weights
+ * directly (no cache).
+ *
+ * mq_quantize_q8_1: for each row m and 32-element block b of X:
+ *   a = max|x|, d = fl32(a / 127), q = the integer nearest fl32(x / d), halves
+ *   away from zero (0 when d = 0), s = fl32(d · Σq);
+ *   Xq[m·ldq + k] = q (int8), ds[2·(m·K/32 + b)] = d, ds[2·(m·K/32 + b) + 1] = s.
+ *   X   : device f32, 16-byte aligned, row stride ldx (>= K, multiple of 4,
+ *         <= MQ_MAX_K); finite values.
+ *   Xq  : device int8, 16-byte aligned, row stride ldq (>= K, multiple of 16,
+ *         <= MQ_MAX_K); columns >= K are not written.
+ *   ds  : device f32, 16-byte aligned, M·K/16 floats.
+ *   K   : multiple of 32.
+ * Errors: MQ_ERR_NULL, MQ_ERR_SHAPE, MQ_ERR_LD, MQ_ERR_ALIGN, MQ_ERR_HIP. */
+int mq_quantize_q8_1(const float *X, int ldx, int8_t *Xq, int ldq, float *ds, int M, int K,
+                     void *stream);
+
+/* Workspace bytes of mq_gemm_mmq (K-split planes; 0 when nothing is split). */
+int64_t mq_gemm_mmq_workspace_bytes(int fmt, int M, int N, int K, int split_k);
+
+/* Y[M×N] = the int8 product of mq_quantize_q8_1's (Xq, ds) and Wq:
+ *   each format is split as w = α·c − β (int8 code c, f32 factors exact per
+ *   32-element group, per 16 for Q6_K: Q8_0 α = d, c = q; Q4_0 c = q − 8;
+ *   Q5_0 c = q − 16; Q5_1 c = q, β = −m; Q4_K / Q5_K α = d·sc, β = dmin·m;
+ *   Q6_K α = d·s, c = q − 32), and
+ *   Y[m, n] = Σ_b (d_b · Σ_G α_G · I_G − β_b · s_b),  I_G = Σ_{i∈G} c_i·q_i
+ *   with I exact (int8 MFMA, i32 accumulation) and the rest in f32.
+ * Accuracy contract: |Y − Y_exact| <= 1e-3·S + 1e-5 per element, Y_exact and
+ * S = Σ_b (Σ_G |d α I_G| + |β s|) evaluated exactly from the same integers
+ * and factors.
+ *   fmt : any MQ_Q* format; K a multiple of its block (and of 32).
+ *   Xq, ldq, ds : as written by mq_quantize_q8_1 for these M and K.
+ *   wq  : device, 16-byte aligned, N·mq_row_bytes(fmt, K) bytes.
+ *   Y, ldy, ws, ws_bytes, split_k, stream : as mq_gemm_fused, with
+ *         ws_bytes >= mq_gemm_mmq_workspace_bytes(fmt, M, N, K, split_k). */
+int mq_gemm_mmq(int fmt, const int8_t *Xq, int ldq, const float *ds, const void *wq, float *Y,
+                int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
+                void *stream);
+
 /* Static text for a return code (never NULL). */
 const char *mq_strerror(int code);
 

@@ -28,6 +28,9 @@ from .api import (
     dequant_to_f16_batch,
     gemm_f16cache,
     gemm_fused,
+    gemm_mmq,
+    mmq_workspace_bytes,
+    quantize_q8_1,
     row_bytes,
     workspace_bytes,
 )
@@ -51,7 +54,10 @@ __all__ = [
     "dequant_to_f16_batch",
     "gemm_f16cache",
     "gemm_fused",
+    "gemm_mmq",
     "lib",
+    "mmq_workspace_bytes",
+    "quantize_q8_1",
     "row_bytes",
     "workspace_bytes",
 ]

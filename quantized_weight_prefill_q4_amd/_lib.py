@@ -57,6 +57,10 @@ SIGNATURES = {
     "mq_gemm_fused_xf32": (_c_int, [_c_int, _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
                                     _c_int, _vp, _c_size, _c_int, _vp]),
     "mq_convert_f32_to_f16": (_c_int, [_vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp]),
+    "mq_quantize_q8_1": (_c_int, [_vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _vp]),
+    "mq_gemm_mmq_workspace_bytes": (_c_i64, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "mq_gemm_mmq": (_c_int, [_c_int, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                             _vp, _c_size, _c_int, _vp]),
     "mq_strerror": (ctypes.c_char_p, [_c_int]),
     "mq_last_hip_error": (_c_int, []),
 }

@@ -198,3 +198,60 @@ def convert_f32_to_f16(x: torch.Tensor, K: int | None = None,
     check(lib().mq_convert_f32_to_f16(x.data_ptr(), ldx, out.data_ptr(), ld16, M, K, _stream(x)),
           "mq_convert_f32_to_f16")
     return out
+
+
+def quantize_q8_1(x: torch.Tensor, K: int | None = None, xq: torch.Tensor | None = None,
+                  ds: torch.Tensor | None = None):
+    """Q8_1-style int8 blocks of the f32 activations x[:, :K]: (codes int8
+    [M, ldq], factors f32 [M, K/32, 2] = (d, s) per 32-element block)."""
+    _need_cuda(x, "x", torch.float32)
+    ldx = _row_major_2d(x, "x")
+    M = x.shape[0]
+    K = x.shape[1] if K is None else K
+    if xq is None:
+        xq = torch.empty((M, (K + 15) // 16 * 16), dtype=torch.int8, device=x.device)
+    else:
+        _need_cuda(xq, "xq", torch.int8)
+    ldq = _row_major_2d(xq, "xq")
+    if ds is None:
+        ds = torch.empty((M, K // 32, 2), dtype=torch.float32, device=x.device)
+    else:
+        _need_cuda(ds, "ds", torch.float32)
+        if not ds.is_contiguous() or ds.numel() < M * (K // 32) * 2:
+            raise ValueError("ds must be contiguous with M*K/16 floats")
+    check(lib().mq_quantize_q8_1(x.data_ptr(), ldx, xq.data_ptr(), ldq, ds.data_ptr(), M, K,
+                                 _stream(x)), "mq_quantize_q8_1")
+    return xq, ds
+
+
+def mmq_workspace_bytes(fmt, M: int, N: int, K: int, split_k: int = 0) -> int:
+    return check(lib().mq_gemm_mmq_workspace_bytes(_fmt(fmt), M, N, K, split_k),
+                 "mq_gemm_mmq_workspace_bytes")
+
+
+def gemm_mmq(xq: torch.Tensor, ds: torch.Tensor, wq: torch.Tensor, fmt, N: int, K: int,
+             split_k: int = 0, out: torch.Tensor | None = None,
+             ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] (f32): the int8 product of quantize_q8_1's (xq, ds) and the
+    quantized weight wq (rows contiguous)."""
+    f = _fmt(fmt)
+    _need_cuda(xq, "xq", torch.int8)
+    _need_cuda(ds, "ds", torch.float32)
+    _need_cuda(wq, "wq", torch.uint8)
+    if not wq.is_contiguous() or not ds.is_contiguous():
+        raise ValueError("wq and ds must be contiguous")
+    ldq = _row_major_2d(xq, "xq")
+    M = xq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    else:
+        _need_cuda(out, "out", torch.float32)
+    ldy = _row_major_2d(out, "out")
+    if ws is None:
+        nbytes = mmq_workspace_bytes(f, M, N, K, split_k)
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device=xq.device) if nbytes else None
+    check(lib().mq_gemm_mmq(f, xq.data_ptr(), ldq, ds.data_ptr(), wq.data_ptr(), out.data_ptr(),
+                            ldy, M, N, K, 0 if ws is None else ws.data_ptr(),
+                            0 if ws is None else ws.numel() * ws.element_size(), split_k,
+                            _stream(xq)), "mq_gemm_mmq")
+    return out

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libmq.so")
-SOURCES = ("mq_api.hip", "dequant.hip", "gemm.hip", "gemm_xf32.hip")
+SOURCES = ("mq_api.hip", "dequant.hip", "gemm.hip", "gemm_xf32.hip", "mmq.hip")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

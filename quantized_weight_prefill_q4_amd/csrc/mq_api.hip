@@ -25,6 +25,9 @@ int check_dims(int M, int N, int K) {
 
 bool ld_ok(int64_t ld, int64_t K) { return ld >= K && ld % 8 == 0 && ld <= MQ_MAX_K + 64; }
 
+// int8 code rows: 16-byte aligned, at most MQ_MAX_K bytes apart.
+bool ldq_ok(int64_t ld, int64_t K) { return ld >= K && ld % 16 == 0 && ld <= MQ_MAX_K; }
+
 // f32 activation rows: 16-byte aligned (ld a multiple of 4), at most MQ_MAX_K
 // elements apart (a 256-row tile then spans at most 2^31 bytes).
 bool ld32_ok(int64_t ld, int64_t K) { return ld >= K && ld % 4 == 0 && ld <= MQ_MAX_K; }
@@ -244,13 +247,50 @@ int mq_convert_f32_to_f16(const float *X, int ldx, uint16_t *X16, int ld16, int 
     return hip_status(mq::launch_convert_f32_to_f16(X, ldx, X16, ld16, M, K, (hipStream_t)stream));
 }
 
+int mq_quantize_q8_1(const float *X, int ldx, int8_t *Xq, int ldq, float *ds, int M, int K,
+                     void *stream) {
+    if (!X || !Xq || !ds) return MQ_ERR_NULL;
+    if (check_dims(M, 1, K) || K % 32) return MQ_ERR_SHAPE;
+    if (!ld32_ok(ldx, K) || !ldq_ok(ldq, K)) return MQ_ERR_LD;
+    if (!aligned16(X) || !aligned16(Xq) || !aligned16(ds)) return MQ_ERR_ALIGN;
+    return hip_status(mq::launch_quantize_q8_1(X, ldx, Xq, ldq, ds, M, K, (hipStream_t)stream));
+}
+
+int64_t mq_gemm_mmq_workspace_bytes(int fmt, int M, int N, int K, int split_k) {
+    if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    if (int rc = check_dims(M, N, K)) return rc;
+    if (K % mq::block_elems(fmt) || K % 32) return MQ_ERR_SHAPE;
+    if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
+    if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
+    return mq::plan_mmq(M, N, K, split_k).ws_bytes;
+}
+
+int mq_gemm_mmq(int fmt, const int8_t *Xq, int ldq, const float *ds, const void *wq, float *Y,
+                int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
+                void *stream) {
+    if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    if (!Xq || !ds || !wq || !Y) return MQ_ERR_NULL;
+    if (int rc = check_dims(M, N, K)) return rc;
+    if (K % mq::block_elems(fmt) || K % 32) return MQ_ERR_SHAPE;
+    if (!ldq_ok(ldq, K) || ldy < N) return MQ_ERR_LD;
+    if (!aligned16(Xq) || !aligned16(ds) || !aligned16(wq) || !aligned16(Y)) return MQ_ERR_ALIGN;
+    if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
+    if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
+    const mq::GemmPlan plan = mq::plan_mmq(M, N, K, split_k);
+    if (plan.ws_bytes > 0 && (!ws || !aligned16(ws) || ws_bytes < (size_t)plan.ws_bytes))
+        return MQ_ERR_WORKSPACE;
+    const int64_t row_bytes = (int64_t)K / mq::block_elems(fmt) * mq::block_bytes(fmt);
+    return hip_status(mq::launch_mmq(fmt, Xq, ldq, ds, wq, row_bytes, Y, ldy, M, N, K, plan,
+                                     (float *)ws, (hipStream_t)stream));
+}
+
 const char *mq_strerror(int code) {
     switch (code) {
     case MQ_OK: return "success";
     case MQ_ERR_NULL: return "a required pointer is NULL";
     case MQ_ERR_FORMAT: return "unknown weight format";
     case MQ_ERR_SHAPE: return "M, N or K out of range, or K not a multiple of the block size";
-    case MQ_ERR_LD: return "a leading dimension is too small, too large or not a multiple of 8 (4 for f32 rows)";
+    case MQ_ERR_LD: return "a leading dimension is too small, too large or not a multiple of 8 (4 for f32 rows, 16 for int8 codes)";
     case MQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MQ_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than required";
     case MQ_ERR_SPLIT: return "split_k out of range for this problem";

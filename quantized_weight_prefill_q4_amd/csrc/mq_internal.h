@@ -80,6 +80,15 @@ hipError_t launch_gemm_xf32(int fmt, const float *X, int ldx, const void *W, int
                             float *Y, int ldy, int M, int N, int K, const GemmPlan &plan,
                             float *ws, hipStream_t stream);
 
+// The int8 product: Q8_1-style activation blocks (codes Xq, row stride ldq;
+// (d, s) pairs ds, [M][K/32]) and the plan and launch of the MMQ kernel.
+hipError_t launch_quantize_q8_1(const float *X, int ldx, int8_t *Xq, int ldq, float *ds, int M,
+                                int K, hipStream_t stream);
+GemmPlan plan_mmq(int M, int N, int K, int split_req);
+hipError_t launch_mmq(int fmt, const int8_t *Xq, int ldq, const float *ds, const void *W,
+                      int64_t ldw, float *Y, int ldy, int M, int N, int K, const GemmPlan &plan,
+                      float *ws, hipStream_t stream);
+
 // X16[m·ld16 + k] = f16_rne(X[m·ldx + k]) for m < M, k < K (K a multiple of 8).
 hipError_t launch_convert_f32_to_f16(const float *X, int ldx, uint16_t *X16, int ld16, int M,
                                      int K, hipStream_t stream);

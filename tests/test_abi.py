@@ -156,6 +156,38 @@ def test_xf32_entry_points_reject(L):
     assert v(FAKE, 512, MIS, 512, 4, 512, None) == _lib.MQ_ERR_ALIGN
 
 
+def test_mmq_entry_points_reject(L):
+    q = L.mq_quantize_q8_1
+    # (X, ldx, Xq, ldq, ds, M, K, stream)
+    assert q(None, 512, FAKE, 512, FAKE, 4, 512, None) == _lib.MQ_ERR_NULL
+    assert q(FAKE, 512, FAKE, 512, None, 4, 512, None) == _lib.MQ_ERR_NULL
+    assert q(FAKE, 512, FAKE, 512, FAKE, 4, 496, None) == _lib.MQ_ERR_SHAPE      # K % 32
+    assert q(FAKE, 512, FAKE, 512, FAKE, 0, 512, None) == _lib.MQ_ERR_SHAPE
+    assert q(FAKE, 510, FAKE, 512, FAKE, 4, 480, None) == _lib.MQ_ERR_LD         # ldx % 4
+    assert q(FAKE, 512, FAKE, 520, FAKE, 4, 512, None) == _lib.MQ_ERR_LD         # ldq % 16
+    assert q(FAKE, 512, FAKE, 496, FAKE, 4, 512, None) == _lib.MQ_ERR_LD         # ldq < K
+    assert q(FAKE, 512, FAKE, 512, MIS, 4, 512, None) == _lib.MQ_ERR_ALIGN
+    g = L.mq_gemm_mmq
+    # (fmt, Xq, ldq, ds, wq, Y, ldy, M, N, K, ws, wsb, split, stream)
+    assert g(5, FAKE, 512, FAKE, FAKE, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_FORMAT
+    assert g(0, FAKE, 512, FAKE, FAKE, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_FORMAT
+    assert g(12, FAKE, 512, None, FAKE, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_NULL
+    assert g(12, FAKE, 512, FAKE, FAKE, FAKE, 256, 64, 256, 480, None, 0, 1, None) == _lib.MQ_ERR_SHAPE
+    assert g(8, FAKE, 512, FAKE, FAKE, FAKE, 256, 64, 256, 48, None, 0, 1, None) == _lib.MQ_ERR_SHAPE
+    assert g(8, FAKE, 520, FAKE, FAKE, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_LD
+    assert g(8, FAKE, 512, FAKE, FAKE, FAKE, 255, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_LD
+    assert g(14, FAKE, 512, FAKE, MIS, FAKE, 256, 64, 256, 512, None, 0, 1, None) == _lib.MQ_ERR_ALIGN
+    assert g(14, FAKE, 512, FAKE, FAKE, FAKE, 256, 64, 256, 512, None, 0, 17, None) == _lib.MQ_ERR_SPLIT
+    assert g(14, FAKE, 512, FAKE, FAKE, FAKE, 256, 64, 256, 512, None, 0, 4, None) == _lib.MQ_ERR_WORKSPACE
+    w = L.mq_gemm_mmq_workspace_bytes
+    # 128 x 128 tiles, 128-wide k-steps: a forced split of 4 over 4 steps
+    assert w(14, 64, 256, 512, 4) == 4 * 2 * 128 * 128 * 4
+    assert w(12, 2048, 4096, 4096, 0) == 0                 # 512 tiles: two whole rounds
+    # 16 x 33 = 528 tiles: 2 rounds + 16 tiles split min(16, 256/16, 32/2) = 16 ways
+    assert w(12, 2048, 4224, 4096, 0) == 16 * 16 * 128 * 128 * 4
+    assert w(99, 64, 128, 128, 1) == _lib.MQ_ERR_FORMAT
+
+
 def test_dequant_batch_rejects(L):
     J = _lib.MqDequantJob
     ok = J(12, 64, 256, 256, FAKE, FAKE)
