@@ -70,6 +70,8 @@ def parse():
                    help="skip the per-format decode / fused table")
     p.add_argument("--no-xf32", action="store_true",
                    help="skip the f32-activation table")
+    p.add_argument("--mmq-steps", type=int, default=3,
+                   help="steps of the int8-path forward (0 = skip)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="token rows of the oracle sample")
@@ -77,6 +79,8 @@ def parse():
                    help="layers (7 matrices each) of the oracle sample")
     p.add_argument("--only-shape", default=None,
                    help="profiling aid: run only this 7B matrix's cache GEMM --steps times")
+    p.add_argument("--only-mmq", default=None,
+                   help="time only this 7B shape on the int8 path (for counter runs)")
     p.add_argument("--only-load", action="store_true",
                    help="profiling aid: run only the batched decode of the 7B weight set --steps times")
     p.add_argument("--calib-copy", action="store_true",
@@ -131,6 +135,32 @@ def run_only_shape(torch, mq, name, steps, dev):
                       "median_call_us": round(us, 2),
                       "tflops": round(2.0 * M * N * K / us / 1e6, 1),
                       "algorithmic_bytes_per_call": M * K * 2 + N * K * 2 + M * N * 4}), flush=True)
+
+
+def run_only_mmq(torch, mq, name, steps, dev):
+    """One 7B shape on the int8 path at M = 2048 (activations quantized once
+    beforehand), for counter runs of the MMQ kernel alone."""
+    fmt, N, K = next((f, n, k) for nm, f, n, k in synth.LAYER_7B if nm == name)
+    M = 2048
+    q = synth.weights_device(fmt, 1, N, K, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    x = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32)
+    xq, ds = mq.quantize_q8_1(x)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws_n = mq.mmq_workspace_bytes(fmt, M, N, K)
+    ws = torch.empty(max(1, ws_n // 4), dtype=torch.float32, device=dev)
+    mq.gemm_mmq(xq, ds, q, fmt, N, K, out=y, ws=ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record()
+        mq.gemm_mmq(xq, ds, q, fmt, N, K, out=y, ws=ws)
+    ev[steps].record()
+    torch.cuda.synchronize()
+    us = statistics.median(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+    print(json.dumps({"only_mmq": name, "M": M, "N": N, "K": K, "calls": steps + 1,
+                      "median_call_us": round(us, 2),
+                      "tops": round(2.0 * M * N * K / us / 1e6, 1)}), flush=True)
 
 
 def run_calib_copy(torch, steps, dev):
@@ -289,12 +319,16 @@ def _median_us(torch, fn, reps, warm=2):
 def formats_table(torch, mq, dev, log_rows):
     """Every weight format on one shape (N = 14336, K = 4096, the Llama-3.1-8B
     gate/up projection): load-time decode GB/s (quantized bytes read + f16
-    cache written) and the fused GEMM at M = 128 and 2048, beside the cache
-    GEMM on the same shape.  Weight copies rotate over > 512 MB."""
+    cache written), the fused GEMM and the int8 product at M = 128 and 2048
+    (activations quantized beforehand; the quantize time is listed once),
+    beside the cache GEMM on the same shape.  Weight copies rotate over
+    > 512 MB."""
     N, K = 14336, 4096
     x = synth.activations_device(6100, 2048, K, dev)
+    xq, xds = mq.quantize_q8_1(x.float())
     out = {}
     cache_us = {}
+    quant_us = {}
     for fi, (fname, fmt) in enumerate(sorted(mq.FORMATS.items(), key=lambda kv: kv[1])):
         q0 = synth.weights_device(fmt, 6200 + fi, N, K, dev)
         nq = max(3, -(-512 * 2 ** 20 // q0.numel()))
@@ -314,6 +348,15 @@ def formats_table(torch, mq, dev, log_rows):
             t = _median_us(torch, lambda r: mq.gemm_fused(xm, qs[r % nq], fmt, N, K, out=y, ws=ws), 12)
             rec[f"fused_m{M}_us"] = round(t, 2)
             rec[f"fused_m{M}_tflops"] = round(2.0 * M * N * K / t / 1e6, 1)
+            wsm = torch.empty(max(1, mq.mmq_workspace_bytes(fmt, M, N, K) // 4),
+                              dtype=torch.float32, device=dev)
+            qm, dm = xq[:M], xds[:M]
+            t = _median_us(torch, lambda r: mq.gemm_mmq(qm, dm, qs[r % nq], fmt, N, K, out=y, ws=wsm), 12)
+            rec[f"mmq_m{M}_us"] = round(t, 2)
+            rec[f"mmq_m{M}_tops"] = round(2.0 * M * N * K / t / 1e6, 1)
+            if M not in quant_us:
+                xm32 = x[:M].float()
+                quant_us[M] = _median_us(torch, lambda r: mq.quantize_q8_1(xm32, xq=qm, ds=dm), 12)
             if M not in cache_us:
                 wsc = torch.empty(max(1, mq.workspace_bytes(0, M, N, K) // 4), dtype=torch.float32,
                                   device=dev)
@@ -322,14 +365,18 @@ def formats_table(torch, mq, dev, log_rows):
         out[fname] = rec
         log_rows.append(f"  {fname:5s} {rec['quant_bytes'] / 2 ** 20:6.1f} MiB  decode {t_deq:7.1f} us "
                         f"{rec['dequant_gbs']:6.0f} GB/s   fused M=128 {rec['fused_m128_us']:7.1f} us "
-                        f"({rec['fused_m128_tflops']:6.1f} TF/s)  M=2048 {rec['fused_m2048_us']:7.1f} us "
-                        f"({rec['fused_m2048_tflops']:6.1f} TF/s)")
+                        f"M=2048 {rec['fused_m2048_us']:7.1f} us ({rec['fused_m2048_tflops']:6.1f} TF/s)"
+                        f"   int8 M=128 {rec['mmq_m128_us']:7.1f} us M=2048 {rec['mmq_m2048_us']:7.1f} us"
+                        f" ({rec['mmq_m2048_tops']:6.1f} TOP/s)")
         del qs, q0, caches
         torch.cuda.empty_cache()
     out["cache_gemm"] = {f"m{M}_us": round(t, 2) for M, t in cache_us.items()}
+    out["quantize_q8_1"] = {f"m{M}_us": round(t, 2) for M, t in quant_us.items()}
     log_rows.append("  cache GEMM on the same shape: " +
                     ", ".join(f"M={M} {t:.1f} us ({2.0 * M * N * K / t / 1e6:.1f} TF/s)"
-                              for M, t in cache_us.items()))
+                              for M, t in cache_us.items()) +
+                    "; activation quantize (f32 -> int8 blocks): " +
+                    ", ".join(f"M={M} {t:.1f} us" for M, t in quant_us.items()))
     return out
 
 
@@ -386,6 +433,54 @@ def xf32_table(torch, mq, dev, log_rows):
     del qs, caches, x32, x16
     torch.cuda.empty_cache()
     return out
+
+
+def mmq_forward(torch, mq, W, M, steps, dev):
+    """The 196 GEMMs of the forward on the int8 path: per layer the four
+    distinct inputs (q|k|v, o, gate|up, down; f32) are quantized once each to
+    Q8_1-style blocks, then the seven products read the quantized weights
+    directly.  Returns (median ms per step, median ms of its quantize calls)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(7003)
+    xa = torch.randn((M, 3584), generator=g, device=dev, dtype=torch.float32)
+    xf = torch.randn((M, 18944), generator=g, device=dev, dtype=torch.float32)
+    qa, da = mq.quantize_q8_1(xa)
+    qf, df = mq.quantize_q8_1(xf)
+    ys = {n: torch.empty((M, N), dtype=torch.float32, device=dev) for n, _, N, _ in synth.LAYER_7B}
+    wsb = max(mq.mmq_workspace_bytes(f, M, N, K) for _, f, N, K in synth.LAYER_7B)
+    ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
+
+    def step(evq=None):
+        for row in W:
+            for name in ("q", "k", "v", "o", "gate", "up", "down"):
+                fmt, N, K, q, _ = row[name]
+                if name in ("q", "o", "gate", "down"):      # a new layer input
+                    x, xq, ds = (xf, qf, df) if name == "down" else (xa, qa, da)
+                    mq.quantize_q8_1(x, xq=xq, ds=ds)
+                xq, ds = (qf, df) if name == "down" else (qa, da)
+                mq.gemm_mmq(xq, ds, q, fmt, N, K, out=ys[name], ws=ws)
+
+    step()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        evs[i].record()
+        step()
+    evs[steps].record()
+    torch.cuda.synchronize()
+    d = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    # the quantize calls alone, as in one step (4 per layer)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(len(W)):
+        mq.quantize_q8_1(xa, xq=qa, ds=da)
+        mq.quantize_q8_1(xa, xq=qa, ds=da)
+        mq.quantize_q8_1(xa, xq=qa, ds=da)
+        mq.quantize_q8_1(xf, xq=qf, ds=df)
+    b.record()
+    torch.cuda.synchronize()
+    qms = a.elapsed_time(b)
+    del xa, xf, qa, qf, ys, ws
+    return statistics.median(d), qms
 
 
 def grouped_forward(torch, mq, W, xa, xf, steps, dev):
@@ -529,6 +624,9 @@ def main():
     if args.only_shape:
         run_only_shape(torch, mq, args.only_shape, args.steps, dev)
         return
+    if args.only_mmq:
+        run_only_mmq(torch, mq, args.only_mmq, args.steps, dev)
+        return
     if args.only_load:
         W = make_weights(torch, mq, args.layers, dev)
         jobs = [(q, fmt, N, K, cache) for row in W for fmt, N, K, q, cache in row.values()]
@@ -628,6 +726,17 @@ def main():
             f"{grouped['tok_s']:.0f} tok/s, {grouped['tflops']:.0f} TFLOP/s")
         torch.cuda.empty_cache()
 
+    # -- int8 (MMQ) forward ----------------------------------------------------------
+    mmqf = None
+    if args.mmq_steps > 0:
+        m_ms, q_ms = mmq_forward(torch, mq, W, M, args.mmq_steps, dev)
+        mmqf = {"ms_per_step": round(m_ms, 3), "tok_s": round(M / (m_ms / 1e3), 1),
+                "tops": round(flops.sum() / (m_ms / 1e3) / 1e12, 1),
+                "quantize_ms_per_step": round(q_ms, 3)}
+        log(f"[bench] int8 (MMQ) forward: {m_ms:.3f} ms/step, {mmqf['tok_s']:.0f} tok/s, "
+            f"{mmqf['tops']:.0f} TOP/s (of which {q_ms:.3f} ms quantizing activations)")
+        torch.cuda.empty_cache()
+
     # -- fused forward (no cache) ---------------------------------------------------
     fused = None
     if args.fused_steps > 0:
@@ -721,6 +830,7 @@ def main():
             "frac": round(deq_gbs / PEAK_HBM_GBS, 4),
         },
         "fused": fused,
+        "mmq_forward": mmqf,
         "grouped_forward": grouped,
         "crossover": cross,
         "formats": fmts,

@@ -18,11 +18,16 @@
 // 128 (four activation blocks).  The codes of both operands sit in LDS as
 // 128-byte rows of eight 16-byte chunks, swizzled as the f16 kernels' tiles;
 // the per-block factors sit beside them, (d, s) per activation row and
-// (α, β) — (α_lo, α_hi) for Q6_K — per weight row.  Per block and 32×32
+// (α, β) per weight row — for Q6_K (d, the two int8 group scales).  Per block and 32×32
 // fragment: one v_mfma_i32_32x32x32_i8 (two v_mfma_i32_32x32x16_i8 for Q6_K,
-// one per scale group), then acc += float(I)·(d·α) [− β·s] on the VALU.
-// The per-block scaling costs ~3 VALU operations per output per 32 k against
-// 64 int8 multiply-adds in the matrix core, so this kernel is VALU-bound.
+// one per scale group, combined as I0·s0 + I1·s1 in integers), then
+// acc += float(I)·(d·α) on the VALU; the
+// β·s terms of two blocks at a time go through one v_mfma_f32_32x32x2_f32
+// (s of the rows against −β of the columns), on the matrix core the int8
+// products leave mostly idle.  The per-block scaling still costs 3 VALU
+// operations per output per 32 k against 64 int8 multiply-adds in the
+// matrix core, so this kernel is VALU-bound.  (The file is compiled with
+// MFMA results in VGPRs: the VALU reads them directly.)
 
 #include "gemm_kernel.h"
 
@@ -34,6 +39,7 @@ constexpr int kMmqKB = kMmqBK / 32;   // activation blocks per step
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
@@ -430,8 +436,14 @@ struct MmqBQ6Loader {
         }
         const uint32_t sc = __builtin_amdgcn_alignbyte(tail[i][1], tail[i][0], s);
         const float d = f16_bits_to_f32(s ? tail[i][2] >> 16 : tail[i][2]);
-        const float a0 = d * (float)(int8_t)(sc & 255), a1 = d * (float)(int8_t)((sc >> 8) & 255);
-        const float a2 = d * (float)(int8_t)((sc >> 16) & 255), a3 = d * (float)(int8_t)(sc >> 24);
+        // factors per 32-element block: d and the two int8 group scales,
+        // sign-extended into the halves of one word (the kernel combines the
+        // two group dots in integers: I0·s0 + I1·s1, exact)
+        auto pair = [](uint32_t lo, uint32_t hi) {
+            return __builtin_bit_cast(float, (uint32_t)(int)(int8_t)lo & 0xFFFFu |
+                                                 ((uint32_t)(int)(int8_t)hi << 16));
+        };
+        const float p01 = pair(sc & 255, (sc >> 8) & 255), p23 = pair((sc >> 16) & 255, sc >> 24);
         u32x4 c0 = u32x4{e[0], e[1], e[2], e[3]}, c1 = u32x4{e[4], e[5], e[6], e[7]};
         u32x4 c2 = u32x4{e[8], e[9], e[10], e[11]}, c3 = u32x4{e[12], e[13], e[14], e[15]};
         perm_q6(c0, c1);
@@ -441,8 +453,8 @@ struct MmqBQ6Loader {
         codes[r * 8 + ((4 * p + 1) ^ sw)] = c1;
         codes[r * 8 + ((4 * p + 2) ^ sw)] = c2;
         codes[r * 8 + ((4 * p + 3) ^ sw)] = c3;
-        fac[(2 * p) * ROWS + r] = float2{a0, a1};
-        fac[(2 * p + 1) * ROWS + r] = float2{a2, a3};
+        fac[(2 * p) * ROWS + r] = float2{d, p01};
+        fac[(2 * p + 1) * ROWS + r] = float2{d, p23};
     }
 };
 
@@ -544,18 +556,35 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_kernel(MmqArgs a) {
                 bq[j] = __builtin_bit_cast(v4i, B[r * 8 + (ch ^ swz<8>(r))]);
                 bfac[j] = BF[kb * BN + r];
             }
+            // One fragment at a time: its integer product, then its scaling.
+            // (Issuing all of a block's products first needs 64 more VGPRs
+            // and halves the waves per SIMD, which measured 1.4x slower: the
+            // second wave hides each MFMA's latency better.)
+            auto beta = [&](int i, int j) MQ_INLINE {
+                if constexpr (BETA && (kb & 1)) {
+                    // β·s of blocks kb − 1 (lanes 0–31) and kb (32–63)
+                    const int rs = wm * TM + 32 * i + rl, cs = wn * TN + 32 * j + rl;
+                    const float sa = AF[(kb - 1 + hl) * BM + rs].y;
+                    const float nb = -BF[(kb - 1 + hl) * BN + cs].y;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(sa, nb, acc[i][j], 0, 0, 0);
+                }
+                // the scaled accumulator is "used" here, in program order:
+                // arithmetic carries no ordering against the scheduling
+                // barrier, and left free the compiler issues every block's
+                // MFMAs first and holds all their results at once
+                asm volatile("" : "+v"(acc[i][j]));
+            };
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                // (d, s) of the 16 rows this lane holds in a 32x32 block:
-                // rows 8·(e/4) + 4·hl + e%4, four runs of 4 consecutive rows
-                float dr[16], sr[16];
+                // d of the 16 rows this lane holds in a 32x32 block: rows
+                // 8·(e/4) + 4·hl + e%4, four runs of 4 consecutive rows
+                float dr[16];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int r0 = wm * TM + 32 * i + 8 * g + 4 * hl;
                     const f32x4 p0 = *reinterpret_cast<const f32x4 *>(&AF[kb * BM + r0]);
                     const f32x4 p1 = *reinterpret_cast<const f32x4 *>(&AF[kb * BM + r0 + 2]);
-                    dr[4 * g] = p0.x; sr[4 * g] = p0.y; dr[4 * g + 1] = p0.z; sr[4 * g + 1] = p0.w;
-                    dr[4 * g + 2] = p1.x; sr[4 * g + 2] = p1.y; dr[4 * g + 3] = p1.z; sr[4 * g + 3] = p1.w;
+                    dr[4 * g] = p0.x; dr[4 * g + 1] = p0.z; dr[4 * g + 2] = p1.x; dr[4 * g + 3] = p1.z;
                 }
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
@@ -566,25 +595,22 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_kernel(MmqArgs a) {
                         const long bhi = __builtin_bit_cast(long, int2{bq[j].z, bq[j].w});
                         const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(alo, blo, v16i{}, 0, 0, 0);
                         const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(ahi, bhi, v16i{}, 0, 0, 0);
+                        // |I| <= 16·127·32 and |s| <= 32: 24-bit products, and
+                        // I0·s0 + I1·s1 < 2^24 converts exactly
+                        const int s01 = __builtin_bit_cast(int, bfac[j].y);
+                        const int s0 = (s01 << 16) >> 16, s1 = s01 >> 16;
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
-                            acc[i][j][e] = __builtin_fmaf((float)I0[e], dr[e] * bfac[j].x, acc[i][j][e]);
-                            acc[i][j][e] = __builtin_fmaf((float)I1[e], dr[e] * bfac[j].y, acc[i][j][e]);
+                            const int t = __mul24(I0[e], s0) + __mul24(I1[e], s1);
+                            acc[i][j][e] = __builtin_fmaf((float)t, dr[e] * bfac[j].x, acc[i][j][e]);
                         }
                     } else {
                         const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bq[j], v16i{}, 0, 0, 0);
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) {
+                        for (int e = 0; e < 16; ++e)
                             acc[i][j][e] = __builtin_fmaf((float)I[e], dr[e] * bfac[j].x, acc[i][j][e]);
-                            if constexpr (BETA)
-                                acc[i][j][e] = __builtin_fmaf(-bfac[j].y, sr[e], acc[i][j][e]);
-                        }
                     }
-                    // the scaled accumulator is "used" here, in program order:
-                    // arithmetic carries no ordering against the scheduling
-                    // barrier, and left free the compiler issues every
-                    // block's MFMAs first and holds all their results at once
-                    asm volatile("" : "+v"(acc[i][j]));
+                    beta(i, j);
                 }
             }
         });
