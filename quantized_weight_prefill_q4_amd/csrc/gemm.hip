@@ -10,14 +10,28 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
     GemmPlan p;
     p.bn = 128;
     p.bm = M > 128 ? 256 : (M > 64 ? 128 : 64);
-    // With at least one full round of 256 × 256 tiles the larger tile is used
-    // (half the operand bytes per flop through L2 and LDS): for f16
-    // activations with the f16 cache or a fused format other than Q6_K.  Q6_K's
-    // raw-byte registers, and f32 activation registers, do not fit beside 256
-    // accumulators.
-    if (!x_f32 && fmt != kFmtQ6_K && M > 128 &&
-        (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= kCUs)
-        p.bn = 256;
+    // The larger 256 × 256 tile moves half the operand bytes per flop through
+    // L2 and LDS, which under this part's power limit is time.  It is used
+    // with at least one full round of such tiles, or — when even the
+    // 256 × 128 grid is less than one round — when fewer 256 × 256 tiles split
+    // along K fill at least 7/8 of the compute units while every K range
+    // keeps >= 4096 elements (the partial tiles' write, read and reduce are
+    // then a small part of the call: the 7B down shape, 3584 × 18944, runs
+    // 7% faster than on 224 unsplit 256 × 128 tiles; q/o, K = 3584, would
+    // run 18% slower).  Only for f16 activations with the f16 cache or a
+    // fused format other than Q6_K: Q6_K's raw-byte registers, and f32
+    // activation registers, do not fit beside 256 accumulators.
+    if (!x_f32 && fmt != kFmtQ6_K && M > 128) {
+        const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+        const int k64 = (K + 63) / 64;
+        int s = t256 >= kCUs ? 1 : (int)(kCUs / t256);
+        s = s > 16 ? 16 : s;
+        s = s > k64 / 4 ? k64 / 4 : s;
+        const int64_t t128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
+        const bool split_fills =
+            t128 < kCUs && s >= 2 && t256 * s >= kCUs * 7 / 8 && K / s >= 4096;
+        if (t256 >= kCUs || split_fills) p.bn = 256;
+    }
     p.tiles_m = (M + p.bm - 1) / p.bm;
     p.tiles_n = (N + p.bn - 1) / p.bn;
     const int tiles = p.tiles_m * p.tiles_n;

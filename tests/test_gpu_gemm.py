@@ -194,3 +194,20 @@ def test_grouped_shared_input_gemm_exact():
         Ys = to_host(mq.gemm_f16cache(to_dev_f16(x), c, K))
         assert np.array_equal(Ys, Yg[:, r0:r0 + n])
         r0 += n
+
+
+def test_split_256_tiles_for_sub_round_grids_exact():
+    """M = 2048, N = 3584, K = 8192: the 256 × 128 grid (224 tiles) is less than
+    one round, so the plan takes 112 tiles of 256 × 256 split twice along K
+    (4096 k per range; the 7B down shape's plan).  Small-integer operands keep
+    every partial sum exact, so sampled rows across all tiles equal the oracle,
+    and the workspace is the two partial planes of every tile."""
+    M, N, K = 2048, 3584, 8192
+    assert mq.workspace_bytes(0, M, N, K) == 2 * 112 * 256 * 256 * 4
+    g = np.random.default_rng(27)
+    x = g.integers(-2, 3, (M, K)).astype(np.float16).view(np.uint16)
+    w = g.integers(-3, 4, (N, K)).astype(np.float16).view(np.uint16)
+    Y, _ = _gemm(x, w, K)
+    rows = np.unique(np.concatenate([[0, 255, 256, 1791, 2047], g.choice(M, 11)]))
+    Yref, _ = oracle.gemm_ref(x[rows], w)
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
