@@ -58,7 +58,9 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
         }
     }
     if (split > k64) split = k64;
-    const int per = (k64 + split - 1) / split;
+    int per = (k64 + split - 1) / split;
+    // the fused Q6_K loader pairs k-steps (2j, 2j + 1): ranges start even
+    if (fmt == kFmtQ6_K && (per & 1) && split > 1) ++per;
     split = (k64 + per - 1) / per;   // no empty range
     if (split == 1) dp = tiles;
     p.dp_tiles = dp;

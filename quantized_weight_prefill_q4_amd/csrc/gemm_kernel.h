@@ -313,13 +313,19 @@ __device__ __forceinline__ u32x4 q6k_chunk(uint32_t q0, uint32_t q1, float ds) {
 // ---------------------------------------------------------------------------
 template <int ROWS>
 struct Q6KLoader {
+    // The two quarters of a 128-element half (c4 = 2h, 2h + 1: consecutive
+    // k-steps) use the same ql and qh bytes with other nibbles and bit
+    // pairs.  The even quarter loads them; when its set is written to LDS the
+    // raw dwords are copied into the other set, and the odd quarter loads only
+    // its scales and d.  This needs register set == quarter parity, i.e. every
+    // K range starting at an even k-step (the plan rounds Q6_K ranges so).
     static constexpr int NPART = ROWS * 2 / kThreads;
     __amdgpu_buffer_rsrc_t rs;
     uint32_t roff[NPART];
     uint32_t obase[2];
     int c4[2];
-    uint32_t wa[2][NPART][5], wb[2][NPART][5], wh[2][NPART][5];
-    uint32_t wsa[2][NPART], wsb[2][NPART], wd[2][NPART], osc[2][NPART], odd[2][NPART];
+    mutable uint32_t wa[2][NPART][5], wb[2][NPART][5], wh[2][NPART][5], odd[2][NPART];
+    uint32_t wsa[2][NPART], wsb[2][NPART], wd[2][NPART], osc[2][NPART];
 
     __device__ void init(const uint8_t *W, int64_t row_bytes, int n0, int rows_valid, int) {
         const int64_t start = (int64_t)n0 * row_bytes;
@@ -339,10 +345,12 @@ struct Q6KLoader {
     __device__ __forceinline__ void load(int set, int i) {
         const uint32_t h = c4[set] >> 1, gp = c4[set] & 1, p = (int)threadIdx.x & 1;
         const uint32_t o = roff[i] + obase[set];
-        odd[set][i] = o & 2;
-        load5(rs, o + 64 * h + 16 * p, wa[set][i]);
-        load5(rs, o + 64 * h + 32 + 16 * p, wb[set][i]);
-        load5(rs, o + 128 + 32 * h + 16 * p, wh[set][i]);
+        if ((set & 1) == 0) {                 // even quarter: the raw bytes
+            odd[set][i] = o & 2;
+            load5(rs, o + 64 * h + 16 * p, wa[set][i]);
+            load5(rs, o + 64 * h + 32 + 16 * p, wb[set][i]);
+            load5(rs, o + 128 + 32 * h + 16 * p, wh[set][i]);
+        }
         const uint32_t xs = o + 192 + 8 * h + 4 * gp + p;
         osc[set][i] = xs & 3;
         wsa[set][i] = buf_load4(rs, xs & ~3u);
@@ -377,6 +385,15 @@ struct Q6KLoader {
         row[(2 * p + 1) ^ sw] = q6k_chunk(qa2, qa3, dsa);
         row[(4 + 2 * p) ^ sw] = q6k_chunk(qb0, qb1, dsb);
         row[(5 + 2 * p) ^ sw] = q6k_chunk(qb2, qb3, dsb);
+        if ((set & 1) == 0) {                 // hand the raw bytes to the odd quarter
+#pragma unroll
+            for (int k = 0; k < 5; ++k) {
+                wa[set ^ 1][i][k] = wa[set][i][k];
+                wb[set ^ 1][i][k] = wb[set][i][k];
+                wh[set ^ 1][i][k] = wh[set][i][k];
+            }
+            odd[set ^ 1][i] = odd[set][i];
+        }
     }
 };
 
