@@ -211,3 +211,16 @@ def test_split_256_tiles_for_sub_round_grids_exact():
     rows = np.unique(np.concatenate([[0, 255, 256, 1791, 2047], g.choice(M, 11)]))
     Yref, _ = oracle.gemm_ref(x[rows], w)
     assert np.array_equal(Y[rows].astype(np.float64), Yref)
+
+
+def test_narrow_output_64_row_tiles_exact():
+    """M = 2048, N = 512, K = 1024 (a k/v-like narrow output, short K): 64-row
+    tiles, 128 tiles split twice along K.  Integer operands: exact."""
+    M, N, K = 2048, 512, 1024
+    assert mq.workspace_bytes(0, M, N, K) == 2 * 128 * 64 * 128 * 4
+    g = np.random.default_rng(28)
+    x = g.integers(-2, 3, (M, K)).astype(np.float16).view(np.uint16)
+    w = g.integers(-3, 4, (N, K)).astype(np.float16).view(np.uint16)
+    Y, _ = _gemm(x, w, K)
+    Yref, _ = oracle.gemm_ref(x, w)
+    assert np.array_equal(Y.astype(np.float64), Yref)
