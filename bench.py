@@ -605,7 +605,7 @@ def cpu_baseline(rows: int, n_layers: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the matmul path runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
