@@ -220,11 +220,14 @@ def load_phase(torch, mq, W, reps):
     return best, [(name, fmt, N, K, qb, a.elapsed_time(b)) for name, fmt, N, K, qb, a, b in evs]
 
 
-def forward(mq, W, xa, xf, ys, ws, events=None):
-    """One prefill forward: 196 cache GEMMs (events[i] recorded before call i)."""
+def forward(mq, W, xa, xf, ys, ws, events=None, only=None):
+    """One prefill forward: 196 cache GEMMs (events[i] recorded before call i);
+    with `only`, just the calls of those matrices."""
     i = 0
     for row in W:
         for name, (fmt, N, K, q, cache) in row.items():
+            if only is not None and name not in only:
+                continue
             if events is not None:
                 events[i].record()
             mq.gemm_f16cache(xf if name == "down" else xa, cache, K, out=ys[name], ws=ws)
@@ -537,6 +540,85 @@ def grouped_forward(torch, mq, W, xa, xf, steps, dev):
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
+def clock_sample(torch, fn, seconds=1.0):
+    """Shader clock and socket power while fn() (one forward) runs back to back
+    for about `seconds`: an untimed repeat of the timed step, sampled every
+    ~25 ms by a host thread (amdsmi: per-XCD gfx clock, socket power and power
+    cap; else the sysfs sclk line).  Returns None when neither is readable."""
+    import re
+    import threading
+
+    smi = None
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        smi = (amdsmi, amdsmi.amdsmi_get_processor_handles()[0])
+    except Exception:
+        smi = None
+    sysfs = None
+    for d in sorted(os.listdir("/sys/class/drm")) if os.path.isdir("/sys/class/drm") else []:
+        f = os.path.join("/sys/class/drm", d, "device", "pp_dpm_sclk")
+        if d.startswith("card") and os.path.exists(f):
+            sysfs = f
+            break
+    if smi is None and sysfs is None:
+        return None
+    clocks, power, stop = [], [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                if smi is not None:
+                    m = smi[0].amdsmi_get_gpu_metrics_info(smi[1])
+                    xcd = [c for c in m.get("current_gfxclks") or [] if isinstance(c, int)]
+                    if xcd:
+                        clocks.append(statistics.mean(xcd))
+                    if isinstance(m.get("current_socket_power"), int):
+                        power.append(m["current_socket_power"])
+                else:
+                    hit = re.search(r"(\d+)Mhz \*", open(sysfs).read())
+                    if hit:
+                        clocks.append(int(hit.group(1)))
+            except Exception:
+                pass
+            stop.wait(0.025)
+
+    fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample, daemon=True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    th.start()
+    a.record()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        torch.cuda.synchronize()
+    b.record()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    cap = None
+    if smi is not None:
+        try:
+            cap = smi[0].amdsmi_get_power_cap_info(smi[1]).get("power_cap")
+            cap = round(cap / 1e6) if isinstance(cap, int) and cap > 100000 else cap
+        except Exception:
+            cap = None
+        try:
+            smi[0].amdsmi_shut_down()
+        except Exception:
+            pass
+    if not clocks:
+        return None
+    return {"sclk_mhz_median": round(statistics.median(clocks)), "sclk_mhz_min": round(min(clocks)),
+            "sclk_mhz_max": round(max(clocks)), "samples": len(clocks),
+            "socket_power_w_median": round(statistics.median(power)) if power else None,
+            "power_cap_w": cap, "steps": n, "ms_per_step": round(a.elapsed_time(b) / n, 3),
+            "source": "amdsmi gpu metrics" if smi is not None else sysfs}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -715,6 +797,24 @@ def main():
         f"{ach:.0f} TFLOP/s = {100 * ach / PEAK_F16_TFLOPS:.1f}% of {PEAK_F16_TFLOPS:.0f}, "
         f"avg call {avg_launch_us:.1f} us; traffic {traffic} B/call ({traffic_note})")
 
+    # -- shader clock and power while the step runs (untimed repeat) -------------------
+    # Once over the whole step, once over the roofline kernel's calls alone
+    # (the gate/up GEMMs draw more power than the step's average).
+    clock = None
+    c_fwd = clock_sample(torch, lambda: forward(mq, W, xa, xf, ys, ws))
+    c_dom = clock_sample(torch, lambda: forward(mq, W, xa, xf, ys, ws, only=ROOFLINE_SHAPES))
+    if c_fwd is not None and c_dom is not None:
+        at = PEAK_F16_TFLOPS * c_dom["sclk_mhz_median"] / 2400.0
+        clock = {"forward": c_fwd, "roofline_kernel": c_dom,
+                 "mfma_peak_at_kernel_sclk_tflops": round(at, 1),
+                 "roofline_frac_at_kernel_sclk": round(ach / at, 4)}
+        for what, c in (("the forward", c_fwd), ("gate/up calls only", c_dom)):
+            log(f"[bench] clock during {what}: {c['sclk_mhz_median']} MHz median "
+                f"({c['sclk_mhz_min']}-{c['sclk_mhz_max']}), socket power "
+                f"{c['socket_power_w_median']} W of {c['power_cap_w']} W cap")
+        log(f"[bench] dense f16 peak at the roofline kernel's clock {at:.0f} TFLOP/s; "
+            f"the kernel reaches {100 * ach / at:.1f}% of it")
+
     # -- grouped shared-input forward (q|k|v and gate|up as one GEMM each) ------------
     grouped = None
     if args.grouped_steps > 0:
@@ -825,6 +925,7 @@ def main():
             "launches_per_step": int(len(dom)),
             "algorithmic_bytes_per_call": M * 3584 * 2 + 18944 * 3584 * 2 + M * 18944 * 4,
         },
+        "clock": clock,
         "dequant_roofline": {
             "bound": "hbm", "achieved": round(deq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(deq_gbs / PEAK_HBM_GBS, 4),
