@@ -10,7 +10,8 @@
 // with f32 accumulation, and a K split with fixed-order reduction when the
 // output grid leaves compute units idle.
 //
-// Layout of the work (one 256-thread workgroup = 4 wave64s per output tile):
+// Layout of the work (one workgroup per output tile: 4 wave64s, or 8 for the
+// f16-cache tiles narrower than 256 × 256, see gemm_kernel):
 //   * block tile BM×BN of Y, k-step 64; X and W are both K-contiguous, so
 //     each lane feeds MFMA 8 consecutive k of one row (one 16-byte LDS read);
 //   * X and B tiles are double-buffered in LDS as rows of eight 16-byte
@@ -20,7 +21,8 @@
 //     one step ahead; both are spread between the MFMAs of the current step,
 //     so the address path and LDS stay busy while the matrix cores run, and
 //     only one barrier per k-step is needed;
-//   * the 2×2 waves each own a (BM/2)×(BN/2) sub-tile of 32×32 MFMA blocks;
+//   * the waves (2×2, or 4×2 / 2×4 of 8) each own a sub-tile of 32×32 MFMA
+//     blocks;
 //   * global loads go through buffer resources: rows past M/N and k past K
 //     read as zeros, so ragged edges need no branches in the inner loop;
 //   * workgroup ids are remapped so consecutive tiles (sharing a W panel)
@@ -124,10 +126,10 @@ __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, 
 // f16 tile of ROWS rows × 64 k: 8 chunks of 16 bytes per row.  Thread t
 // takes chunk t % 8 of rows t / 8 + 32·i: a wave load covers 8 whole 128-byte
 // row segments, and the thread's chunk keeps one swizzled LDS position.
-template <int ROWS>
+template <int ROWS, int NTH = kThreads>
 struct F16Loader {
-    static constexpr int NPART = ROWS * 8 / kThreads;
-    static constexpr int RSTEP = kThreads / 8;   // rows between a thread's parts
+    static constexpr int NPART = ROWS * 8 / NTH;
+    static constexpr int RSTEP = NTH / 8;   // rows between a thread's parts
     __amdgpu_buffer_rsrc_t rs;
     uint32_t off0;     // byte offset of the thread's chunk at k = 0
     uint32_t stride;   // bytes between its parts
@@ -729,22 +731,32 @@ __device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x1
 // stage; it also orders the reads of stage j%2 before its refill at the end
 // of step j+1.  A global load thus has from its issue in step j until the
 // second half of step j+1 to arrive.
-// BM × BN: block tile; the 2×2 waves each own a (BM/2)×(BN/2) sub-tile.
+// BM × BN: block tile, split over NWV waves.  NWV = 4 (2×2 waves): one wave
+// per SIMD, whose register file then holds a 128 × 128 sub-tile's 256
+// accumulators (the 256 × 256 tile) or the fused loaders' raw bytes.  NWV = 8
+// (4×2 waves, 2×4 for 64-row tiles): two waves per SIMD for the smaller
+// f16-cache tiles, which are bound by LDS throughput rather than by the
+// matrix cores — the LDS serves about twice the ds_read_b128 bytes per clock
+// with two waves per SIMD issuing (measured 210 vs 109 B/clk per CU), which
+// outweighs the third more fragment reads of the smaller wave tiles.
 // A workgroup either computes a whole tile over all of K or one K range of
 // a tail tile (see the plan); the latter writes its f32 partial tile to the
 // workspace.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int FMT, bool XF32>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Args a) {
+template <int BM, int BN, int FMT, bool XF32, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
+    static_assert(NWV == 4 || (NWV == 8 && BN == 128 && FMT == kFmtF16 && !XF32),
+                  "8 waves: f16-cache tiles of 128 columns");
     constexpr int BK = 64;
-    constexpr int TM = BM / 2, TN = BN / 2;
+    constexpr int WN = NWV == 4 ? 2 : (BM >= 128 ? 2 : 4), WM = NWV / WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int CPR = BK / 8;
     __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
     __shared__ u32x4 B0[BN * CPR], B1[BN * CPR];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     // Workgroups [0, dp_tiles) take whole tiles; the rest take one K range of
     // a tail tile.  Each group is remapped over the XCDs on its own (dp_tiles
     // is a multiple of 8, so the round-robin dealing of both starts at XCD 0).
@@ -765,12 +777,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Args a) {
     const int kt_begin = tail ? part * a.steps_per_split : 0;
     const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
 
-    std::conditional_t<XF32, XF32Loader<BM>, F16Loader<BM>> la;
+    std::conditional_t<XF32, XF32Loader<BM>, F16Loader<BM, 64 * NWV>> la;
     if constexpr (XF32)
         la.init((const float *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
     else
         la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
-    typename BLoaderFor<BN, FMT>::T lb;
+    std::conditional_t<NWV == 4, typename BLoaderFor<BN, FMT>::T, F16Loader<BN, 64 * NWV>> lb;
     if constexpr (FMT == kFmtF16)
         lb.init((const uint16_t *)a.W + n0 * a.ldw, min(BN, a.N - n0), a.ldw, a.K);
     else
@@ -864,13 +876,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Args a) {
     const int col_l = lane & 31, row_l = (lane >> 5) * 4;
     if constexpr (BM == 256) {
         // Full tile, 16-byte-aligned rows: each 32x32 block goes through a
-        // private 32 x 36-float LDS patch of the wave (the first A stage, idle
-        // after the last step) so that every lane then stores 4 consecutive
-        // columns of one row — a quarter of the store instructions of the
-        // column-per-lane layout.
+        // private 32 x 36-float LDS patch of the wave (waves 0-3 in the first
+        // A stage, 4-7 in the second, both idle after the last step) so that
+        // every lane then stores 4 consecutive columns of one row — a quarter
+        // of the store instructions of the column-per-lane layout.
         if (rows >= BM && cols >= BN && (ldo & 3) == 0) {
             constexpr int PS = 36;   // patch row stride in floats (keeps 16-byte rows)
-            float *patch = reinterpret_cast<float *>(A0) + wave * (32 * PS);
+            static_assert(4 * 32 * PS * 4 <= BM * CPR * 16, "patches exceed an A stage");
+            float *patch = reinterpret_cast<float *>(wave < 4 ? A0 : A1) + (wave & 3) * (32 * PS);
             sync_lds();              // every wave is done reading the stages
             const int rr = lane >> 3, cc = 4 * (lane & 7);
 #pragma unroll
@@ -936,7 +949,11 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ w
 
 template <int BM, int BN, int FMT, bool XF32>
 hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, FMT, XF32>), dim3(grid), dim3(kThreads), 0, stream, a);
+    // f16-cache tiles of 128 columns on 8 waves (measured 1.5-4% faster at
+    // M = 128 and on the 7B q/o shape; no slower elsewhere)
+    constexpr int NWV = (BN == 128 && FMT == kFmtF16 && !XF32) ? 8 : 4;
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, FMT, XF32, NWV>), dim3(grid), dim3(64 * NWV), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
