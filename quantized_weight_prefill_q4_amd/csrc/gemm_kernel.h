@@ -722,6 +722,77 @@ __device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x1
     });
 }
 
+// Write a wave's accumulators: a whole tile's part of Y, or a tail range's
+// partial tile to slot (part, tail tile) of the workspace.  C layout of a
+// 32x32 MFMA block: the lane holds column (lane & 31) and rows
+// 8·(r/4) + 4·(lane/32) + r%4 for accumulator element r; rows and columns of
+// a partial tile past M/N hold zeros.  S0, S1: the workgroup's two X stages,
+// idle once the k-loop is done.
+template <int BM, int BN, int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN], bool tail,
+                                           int part, int tile, int m0, int n0, int wm, int wn,
+                                           int lane, int wave, u32x4 *S0, u32x4 *S1) {
+    float *out;
+    int64_t ldo;
+    int rows, cols;
+    if (tail) {
+        out = a.ws + ((int64_t)part * a.tail_tiles + (tile - a.dp_tiles)) * (BM * BN);
+        ldo = BN;
+        rows = BM;
+        cols = BN;
+    } else {
+        out = a.Y + (int64_t)m0 * a.ldy + n0;
+        ldo = a.ldy;
+        rows = a.M - m0;
+        cols = a.N - n0;
+    }
+    const int col_l = lane & 31, row_l = (lane >> 5) * 4;
+    if constexpr (BM == 256) {
+        // Full tile, 16-byte-aligned rows: each 32x32 block goes through a
+        // private 32 x 36-float LDS patch of the wave (waves 0-3 in the first
+        // A stage, 4-7 in the second, both idle after the last step) so that
+        // every lane then stores 4 consecutive columns of one row — a quarter
+        // of the store instructions of the column-per-lane layout.
+        if (rows >= BM && cols >= BN && (ldo & 3) == 0) {
+            constexpr int PS = 36;   // patch row stride in floats (keeps 16-byte rows)
+            static_assert(4 * 32 * PS * 4 <= BM * 8 * 16, "patches exceed an X stage");
+            float *patch = reinterpret_cast<float *>(wave < 4 ? S0 : S1) + (wave & 3) * (32 * PS);
+            sync_lds();              // every wave is done reading the stages
+            const int rr = lane >> 3, cc = 4 * (lane & 7);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        patch[((r >> 2) * 8 + row_l + (r & 3)) * PS + col_l] = acc[i][j][r];
+                    // lanes read what other lanes wrote: the LDS runs one wave's
+                    // instructions in order, so only the compiler must keep them
+                    asm volatile("" ::: "memory");
+                    float *dst = out + (int64_t)(wm * TM + i * 32 + rr) * ldo + wn * TN + j * 32 + cc;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<f32x4 *>(dst + (int64_t)(8 * q) * ldo) =
+                            *reinterpret_cast<const f32x4 *>(patch + (rr + 8 * q) * PS + cc);
+                    asm volatile("" ::: "memory");
+                }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = wn * TN + j * 32 + col_l;
+            if (col >= cols) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * TM + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                if (row < rows) out[row * ldo + col] = acc[i][j][r];
+            }
+        }
+}
+
 // ---------------------------------------------------------------------------
 // The GEMM kernel.  Two LDS stages and two register sets per operand:
 // during step j (MFMAs from LDS stage j%2) each thread issues the global
@@ -855,69 +926,302 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     }
     if (kt < kt_end) step(std::integral_constant<int, 0>(), kt);
 
-    // C layout of a 32x32 MFMA block: lane holds column (lane & 31) and rows
-    // 8·(r/4) + 4·(lane/32) + r%4 for accumulator element r.  A tail range
-    // writes its whole partial tile (rows and columns past M/N hold zeros)
-    // to slot (part, tail tile) of the workspace.
-    float *out;
-    int64_t ldo;
-    int rows, cols;
-    if (tail) {
-        out = a.ws + ((int64_t)part * a.tail_tiles + (tile - a.dp_tiles)) * (BM * BN);
-        ldo = BN;
-        rows = BM;
-        cols = BN;
+    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+}
+
+// ---------------------------------------------------------------------------
+// Fused Q4_K GEMM on 256 × 256 tiles with the weights expanded straight into
+// the MFMA operand registers.
+//
+// In gemm_kernel the fused loaders expand a k-step's B tile once per
+// workgroup and write it to LDS as f16 (32 KB), which the 2×2 waves then read
+// back (64 KB per k-step).  Here the 4 waves are laid out 1 × 4: wave w owns
+// weight rows 64w .. 64w + 63 of the tile and all 256 activation rows, so
+// each weight element is still expanded exactly once per tile, by the lane
+// that feeds it to the MFMA.  The raw super-blocks (144 bytes per weight row)
+// are staged in LDS a whole 256-element super-block at a time — the tile's
+// 256 rows × 144 contiguous bytes, each 16-byte chunk loaded once, so the
+// global loads stay whole cache lines — and each lane reads the 16 quant
+// bytes and the header of its rows per k-step.  B then costs 9 KB of LDS
+// writes and 16 KB of reads per k-step instead of 32 + 64 KB, while the X
+// fragment reads double (every wave reads all 256 rows: 128 KB); the global
+// bytes are the same.  Measured on the 7B gate shape against the 2×2 fused
+// kernel: texture-address stalls −90%, LDS bank conflicts −70%, 2-4% less
+// time; the expansion's VALU work (~2.8 instructions per element) is what
+// remains between this kernel and the f16-cache GEMM.
+//
+// Lane l of wave w feeds weight rows 64w + 32f + (l & 31) (f = 0, 1) at
+// k = 16kk + 8(l >> 5) + 0..7 of k-slice kk, which are, within the k-step's
+// 64-element quarter c4 of the super-block, the low nibbles of quant bytes
+// 32c4 + 8(l >> 5) + 0..7 (kk = 0) and 32c4 + 16 + 8(l >> 5) + 0..7 (kk = 1)
+// with sub-block 2c4's scale and min, and the high nibbles of the same bytes
+// (kk = 2, 3) with sub-block 2c4 + 1's.  The arithmetic is the decode's
+// (q4k_chunk), so the expanded values are the cache's bit for bit, and the
+// MFMAs see the same operands in the same order as the cache kernel's.
+//
+// Pipeline: X as in gemm_kernel (two register sets, two LDS stages, loads
+// two k-steps ahead).  Raw weights: two super-block buffers; during the four
+// k-steps of super-block sb the 2304 chunks of super-block sb + 1 are loaded
+// (9 per thread: 3 in each of the first three steps, one step ahead in a
+// register set) and written to the other buffer, which is not read before
+// the last quarter of super-block sb.  Each k-step reads the next step's raw
+// bytes and expands its first k-slice between its own MFMAs; for the last
+// quarter that is the next super-block, complete since the third quarter's
+// barrier (the fourth quarter writes no part).  K ranges are whole
+// super-blocks.
+// ---------------------------------------------------------------------------
+constexpr int kRbChunks = 256 * 144 / 16;           // 16-byte chunks of a tile super-block
+constexpr int kRbPerThread = kRbChunks / kThreads;  // 9
+static_assert(kRbPerThread * kThreads == kRbChunks, "chunks per thread");
+
+// Chunks [lo, hi) of the thread's 9 belong to part c4 (loaded for step c4).
+template <int C4>
+struct RbPart {
+    static constexpr int lo = C4 * 3 < kRbPerThread ? C4 * 3 : kRbPerThread;
+    static constexpr int hi = (C4 + 1) * 3 < kRbPerThread ? (C4 + 1) * 3 : kRbPerThread;
+};
+
+// Scale and min (as the f32 factors d·sc and dmin·m) of sub-blocks 2c4 and
+// 2c4 + 1 from a super-block header (d, dmin, 12 scale bytes).
+template <int C4>
+__device__ __forceinline__ void q4k_sub_scales(const u32x4 h, float &A0, float &C0, float &A1,
+                                               float &C1) {
+    uint32_t sc0, m0, sc1, m1;
+    if constexpr (C4 < 2) {
+        constexpr int s0 = 16 * C4, s1 = s0 + 8;
+        sc0 = (h.y >> s0) & 63;
+        m0 = (h.z >> s0) & 63;
+        sc1 = (h.y >> s1) & 63;
+        m1 = (h.z >> s1) & 63;
     } else {
-        out = a.Y + (int64_t)m0 * a.ldy + n0;
-        ldo = a.ldy;
-        rows = a.M - m0;
-        cols = a.N - n0;
+        constexpr int s0 = 16 * (C4 - 2), s1 = s0 + 8;
+        sc0 = ((h.w >> s0) & 15) | (((h.y >> (s0 + 6)) & 3) << 4);
+        m0 = ((h.w >> (s0 + 4)) & 15) | (((h.z >> (s0 + 6)) & 3) << 4);
+        sc1 = ((h.w >> s1) & 15) | (((h.y >> (s1 + 6)) & 3) << 4);
+        m1 = ((h.w >> (s1 + 4)) & 15) | (((h.z >> (s1 + 6)) & 3) << 4);
     }
-    const int col_l = lane & 31, row_l = (lane >> 5) * 4;
-    if constexpr (BM == 256) {
-        // Full tile, 16-byte-aligned rows: each 32x32 block goes through a
-        // private 32 x 36-float LDS patch of the wave (waves 0-3 in the first
-        // A stage, 4-7 in the second, both idle after the last step) so that
-        // every lane then stores 4 consecutive columns of one row — a quarter
-        // of the store instructions of the column-per-lane layout.
-        if (rows >= BM && cols >= BN && (ldo & 3) == 0) {
-            constexpr int PS = 36;   // patch row stride in floats (keeps 16-byte rows)
-            static_assert(4 * 32 * PS * 4 <= BM * CPR * 16, "patches exceed an A stage");
-            float *patch = reinterpret_cast<float *>(wave < 4 ? A0 : A1) + (wave & 3) * (32 * PS);
-            sync_lds();              // every wave is done reading the stages
-            const int rr = lane >> 3, cc = 4 * (lane & 7);
+    const float d = f16_bits_to_f32(h.x), dmin = f16_bits_to_f32(h.x >> 16);
+    A0 = d * (float)sc0;
+    C0 = dmin * (float)m0;
+    A1 = d * (float)sc1;
+    C1 = dmin * (float)m1;
+}
+
+// The B fragment of k-slice kk from the lane's quant bytes qa (bytes 8h..)
+// and qb (bytes 16 + 8h..) of the quarter.
+template <int KK>
+__device__ __forceinline__ half8 q4k_frag(u32x2 qa, u32x2 qb, float A0, float C0, float A1,
+                                          float C1) {
+    constexpr uint32_t L = 0x0F0F0F0Fu;
+    const u32x2 q = (KK & 1) ? qb : qa;
+    const uint32_t w0 = (KK < 2) ? (q.x & L) : ((q.x >> 4) & L);
+    const uint32_t w1 = (KK < 2) ? (q.y & L) : ((q.y >> 4) & L);
+    return __builtin_bit_cast(half8, q4k_chunk(w0, w1, KK < 2 ? A0 : A1, KK < 2 ? C0 : C1));
+}
+
+// What a lane needs of its two weight rows for one k-step: the quant bytes
+// (qa: bytes 8h.., qb: bytes 16 + 8h.. of the quarter), the two sub-blocks'
+// factors, and the expanded fragments of k-slice 0.  Read and computed during
+// the previous k-step, so a step starts with its first MFMAs.
+struct RbRaw {
+    u32x2 qa[2], qb[2];
+    float A0[2], C0[2], A1[2], C1[2];
+    half8 bf0[2];
+};
+
+template <int C4>
+__device__ __forceinline__ void rb_fetch(const u32x4 *Bc, int lane, int wave, RbRaw &r) {
+    const int h = lane >> 5;
+    u32x4 hdr[2];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+    for (int f = 0; f < 2; ++f) {
+        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * 9;   // the row's 144 bytes
+        hdr[f] = blk[0];
+        const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk + 1 + 2 * C4);
+        r.qa[f] = q2[h];
+        r.qb[f] = q2[2 + h];
+    }
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
+    for (int f = 0; f < 2; ++f) {
+        q4k_sub_scales<C4>(hdr[f], r.A0[f], r.C0[f], r.A1[f], r.C1[f]);
+        r.bf0[f] = q4k_frag<0>(r.qa[f], r.qb[f], r.A0[f], r.C0[f], r.A1[f], r.C1[f]);
+    }
+}
+
+// One k-step of the wave's 256 × 64 tile from X stage Ac and the raw bytes
+// `cur` (fetched during the previous step); fetches the next step's raw
+// bytes (quarter NC4 of buffer Bnext) into `nxt` between the MFMAs.
+template <int NC4, class Slot>
+__device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32x16 (&acc)[8][2],
+                                        int lane, int wave, const RbRaw &cur, RbRaw &nxt,
+                                        Slot &&slot) {
+    const int h = lane >> 5;
+    half8 af[2][8], bf[2][2];
+    auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
+        constexpr int kk = KKc;
+        const int c = kk * 2 + h;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        patch[((r >> 2) * 8 + row_l + (r & 3)) * PS + col_l] = acc[i][j][r];
-                    // lanes read what other lanes wrote: the LDS runs one wave's
-                    // instructions in order, so only the compiler must keep them
-                    asm volatile("" ::: "memory");
-                    float *dst = out + (int64_t)(wm * TM + i * 32 + rr) * ldo + wn * TN + j * 32 + cc;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<f32x4 *>(dst + (int64_t)(8 * q) * ldo) =
-                            *reinterpret_cast<const f32x4 *>(patch + (rr + 8 * q) * PS + cc);
-                    asm volatile("" ::: "memory");
-                }
-            return;
+        for (int i = 0; i < 8; ++i) {
+            const int r = i * 32 + (lane & 31);
+            dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
         }
+    };
+    load_a(std::integral_constant<int, 0>(), af[0]);
+    bf[0][0] = cur.bf0[0];
+    bf[0][1] = cur.bf0[1];
+    static_for<4>([&](auto KK) MQ_INLINE {
+        constexpr int kk = KK, c = kk & 1;
+        if constexpr (kk + 1 < 4) {
+            load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                bf[c ^ 1][f] = q4k_frag<kk + 1>(cur.qa[f], cur.qb[f], cur.A0[f], cur.C0[f],
+                                                cur.A1[f], cur.C1[f]);
+        } else {
+            rb_fetch<NC4>(Bnext, lane, wave, nxt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<16>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 16 + IJ;
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
+                                                               0);
+            if constexpr (n & 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                slot(std::integral_constant<int, n / 2>());
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    });
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
+    static_assert(FMT == kFmtQ4_K, "Q4_K only");
+    constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
+    constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
+    __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
+    __shared__ u32x4 Bq0[kRbChunks], Bq1[kRbChunks];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = 0, wn = wave;
+    const int pid = blockIdx.x;
+    int tile, part = 0;
+    if (pid < a.dp_tiles) {
+        tile = xcd_remap(pid, a.dp_tiles);
+    } else {
+        const int j = xcd_remap(pid - a.dp_tiles, (int)gridDim.x - a.dp_tiles);
+        const int tt = j % a.tail_tiles;
+        tile = a.dp_tiles + tt;
+        part = j / a.tail_tiles;
     }
+    const bool tail = pid >= a.dp_tiles;
+    int tm, tn;
+    tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    // K ranges are whole super-blocks (the plan's steps_per_split is a
+    // multiple of 4, and K of 256)
+    const int kt_begin = tail ? part * a.steps_per_split : 0;
+    const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
+    const int sb_end = kt_end >> 2;
+
+    F16Loader<BM> la;
+    la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
+    constexpr int NA = decltype(la)::NPART;
+    // raw weight chunks: chunk c = thread + 256·i is byte 16(c mod 9) of the
+    // super-block of tile row c / 9, and lands at LDS chunk c
+    const int rows_valid = min(BN, a.N - n0);
+    const __amdgpu_buffer_rsrc_t rsb =
+        make_rsrc(a.W + (int64_t)n0 * a.ldw, (uint32_t)(rows_valid * a.ldw));
+    uint32_t goff[kRbPerThread];
+#pragma unroll
+    for (int i = 0; i < kRbPerThread; ++i) {
+        const int c = (int)threadIdx.x + kThreads * i, r = c / 9;
+        goff[i] = (uint32_t)(r * a.ldw + 16 * (c - 9 * r));
+    }
+    u32x4 bv[2][3];
+    RbRaw raw[2];   // raw bytes of the current and the next k-step (index P, 1 − P)
+
+    f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = wn * TN + j * 32 + col_l;
-            if (col >= cols) continue;
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    // prologue: super-block kt_begin / 4 whole in its buffer, X step kt_begin
+    // in stage 0, X step kt_begin + 1 and part 0 of the next super-block in
+    // register set 1
+    {
+        const int sb0 = kt_begin >> 2, k0 = kt_begin * BK;
+        u32x4 t[kRbPerThread];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * TM + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-                if (row < rows) out[row * ldo + col] = acc[i][j][r];
-            }
-        }
+        for (int i = 0; i < kRbPerThread; ++i) t[i] = buf_load16(rsb, goff[i] + (uint32_t)sb0 * 144u);
+        la.begin(0, k0, true);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.load(0, i);
+        la.begin(1, k0 + BK, kt_begin + 1 < kt_end);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.load(1, i);
+        const bool nlive = sb0 + 1 < sb_end;
+#pragma unroll
+        for (int i = RbPart<0>::lo; i < RbPart<0>::hi; ++i)
+            bv[1][i - RbPart<0>::lo] = buf_load16(rsb, nlive ? goff[i] + (uint32_t)(sb0 + 1) * 144u : kOOB);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.store(0, i, A0);
+        u32x4 *B = (sb0 & 1) ? Bq1 : Bq0;
+#pragma unroll
+        for (int i = 0; i < kRbPerThread; ++i) B[threadIdx.x + kThreads * i] = t[i];
+        sync_lds();
+        rb_fetch<0>(B, lane, wave, raw[0]);
+    }
+
+    // Step kt (quarter C4, P = C4 & 1): X as in gemm_kernel; raw weights:
+    // slots 0..15 load part (C4 + 1) & 3 of the super-block that step kt + 1
+    // writes into set P, slots 16..31 write set 1 − P (part C4 of super-block
+    // kt / 4 + 1) to that super-block's buffer.
+    auto step = [&](auto C4c, int kt) MQ_INLINE {
+        constexpr int C4 = decltype(C4c)::value, P = C4 & 1;
+        constexpr int LC = (C4 + 1) & 3;
+        constexpr int NL = RbPart<LC>::hi - RbPart<LC>::lo, NS = RbPart<C4>::hi - RbPart<C4>::lo;
+        constexpr int H = 16;
+        u32x4 *An = P ? A0 : A1;
+        const int sb = kt >> 2;
+        const u32x4 *Bc = (sb & 1) ? Bq1 : Bq0;
+        u32x4 *Bn = (sb & 1) ? Bq0 : Bq1;
+        // the next step's raw bytes: this super-block's buffer, or for the
+        // last quarter the next one's, complete since the previous barrier
+        // (the last quarter writes no part)
+        static_assert(RbPart<3>::lo == RbPart<3>::hi, "the last quarter writes no part");
+        const u32x4 *Bnext = C4 == 3 ? Bn : Bc;
+        const int sbl = (kt + 1) / 4 + 1;
+        const uint32_t boff = sbl < sb_end ? (uint32_t)sbl * 144u : kOOB;
+        la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
+        rb_step<(C4 + 1) & 3>(P ? A1 : A0, Bnext, acc, lane, wave, raw[P], raw[1 - P],
+                              [&](auto SL) MQ_INLINE {
+            constexpr int sl = SL, half = sl < H ? sl : sl - H;
+            constexpr int TOT = sl < H ? NA + NL : NA + NS;
+            constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
+            static_for<hi - lo>([&](auto O) MQ_INLINE {
+                constexpr int o = lo + O;
+                if constexpr (sl < H) {
+                    if constexpr (o < NA) la.load(P, o);
+                    else bv[P][o - NA] = buf_load16(
+                        rsb, boff == kOOB ? kOOB : goff[RbPart<LC>::lo + o - NA] + boff);
+                } else {
+                    if constexpr (o < NA) la.store(1 - P, o, An);
+                    else Bn[threadIdx.x + kThreads * (RbPart<C4>::lo + o - NA)] = bv[1 - P][o - NA];
+                }
+            });
+        });
+        sync_lds();
+    };
+    for (int kt = kt_begin; kt < kt_end; kt += 4) {
+        step(std::integral_constant<int, 0>(), kt);
+        step(std::integral_constant<int, 1>(), kt + 1);
+        step(std::integral_constant<int, 2>(), kt + 2);
+        step(std::integral_constant<int, 3>(), kt + 3);
+    }
+
+    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
 }
 
 // Y tile = Σ_s partial[s] in the order s = 0, 1, ..., split − 1, for every
@@ -963,8 +1267,12 @@ hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
 template <int FMT, bool XF32>
 hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t stream) {
     if (bm == 256 && bn == 256) {
-        if constexpr (FMT != kFmtQ6_K && !XF32)
+        if constexpr (FMT == kFmtQ4_K && !XF32) {
+            hipLaunchKernelGGL(gemm_q4k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
+            return hipGetLastError();
+        } else if constexpr (FMT != kFmtQ6_K && !XF32) {
             return launch_tile<256, 256, FMT, XF32>(a, grid, stream);
+        }
     } else if (bm == 256 && bn == 128) {
         return launch_tile<256, 128, FMT, XF32>(a, grid, stream);
     } else if (bm == 128 && bn == 128) {

@@ -222,6 +222,12 @@ def test_workspace_planning(L):
     # every other weight format takes the 256 x 256 fused tiles too
     for fmt in (2, 6, 7, 8, 13):
         assert L.mq_gemm_workspace_bytes(fmt, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
+    # the Q4_K 256 x 256 kernel stages whole super-blocks: its K ranges are
+    # multiples of 4 k-steps, so a requested 7-way split of 20 steps becomes
+    # 5 ranges of 4 (Q8_0, same tiles, keeps 7 ranges of 3, the last of 2)
+    assert L.mq_gemm_workspace_bytes(12, 300, 32768, 1280, 7) == 5 * 256 * 256 * 256 * 4
+    assert L.mq_gemm_workspace_bytes(8, 300, 32768, 1280, 7) == 7 * 256 * 256 * 256 * 4
+    assert L.mq_gemm_workspace_bytes(12, 300, 32768, 1280, 3) == 3 * 256 * 256 * 256 * 4
     # q/o: 224 tiles of 256 x 128, one partial round that a split cannot double
     assert L.mq_gemm_workspace_bytes(0, 2048, 3584, 3584, 0) == 0
     assert L.mq_gemm_workspace_bytes(0, 64, 512, 512, 1) == 0
