@@ -30,7 +30,11 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
         const int64_t t128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
         const bool split_fills =
             t128 < kCUs && s >= 2 && t256 * s >= kCUs * 7 / 8 && K / s >= 4096;
-        if (t256 >= kCUs || split_fills) p.bn = 256;
+        // More than 3/4 of a round of 256 × 256 tiles also takes them, unsplit:
+        // the 256 × 128 grid would be a full round plus a tail of more than
+        // 128 tiles, too many to split (14336 × 4096 at M = 1024: 160 -> 139
+        // us; 18944 × 3584 at M = 768 -13%; fused -10%).
+        if (t256 >= kCUs || split_fills || t256 * 4 > kCUs * 3) p.bn = 256;
     }
     // Narrow outputs (the 256 × 128 grid has at most kCUs / 4 tiles, e.g. the
     // 7B k/v projections, N = 512) with a short K take 64-row tiles: four

@@ -213,6 +213,26 @@ def test_split_256_tiles_for_sub_round_grids_exact():
     assert np.array_equal(Y[rows].astype(np.float64), Yref)
 
 
+def test_three_quarter_round_256_tiles_exact():
+    """M = 1000, N = 14336: 4 × 56 = 224 tiles of 256 × 256 (more than 3/4 of a
+    round), which the plan takes unsplit instead of 448 tiles of 256 × 128; the
+    last M-tile holds 232 rows.  Cache and fused Q4_K paths, integer operands:
+    sampled rows exact, the two paths identical."""
+    M, N, K = 1000, 14336, 768
+    assert mq.workspace_bytes(0, M, N, K) == 0 and mq.workspace_bytes(12, M, N, K) == 0
+    g = np.random.default_rng(29)
+    x = g.integers(-2, 3, (M, K)).astype(np.float16).view(np.uint16)
+    q = synth.weights(synth.Q4_K, synth.rng(29, 0, 12, 0), N, K, mode="integer")
+    w = oracle.dequant_ref(synth.Q4_K, q, N, K)
+    Yc, _ = _gemm(x, w, K)
+    announce("gemm_fused", "Q4_K", f"M={M} N={N} K={K}")
+    Yf = to_host(mq.gemm_fused(to_dev_f16(x), to_dev_u8(q), synth.Q4_K, N, K))
+    assert np.array_equal(Yc, Yf)
+    rows = np.unique(np.concatenate([[0, 255, 767, 768, 999], g.choice(M, 11)]))
+    Yref, _ = oracle.gemm_ref(x[rows], w)
+    assert np.array_equal(Yc[rows].astype(np.float64), Yref)
+
+
 def test_narrow_output_64_row_tiles_exact():
     """M = 2048, N = 512, K = 1024 (a k/v-like narrow output, short K): 64-row
     tiles, 128 tiles split twice along K.  Integer operands: exact."""
