@@ -15,10 +15,11 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
     // with at least one full round of such tiles, or — when even the
     // 256 × 128 grid is less than one round — when fewer 256 × 256 tiles split
     // along K fill at least 7/8 of the compute units while every K range
-    // keeps >= 4096 elements (the partial tiles' write, read and reduce are
+    // keeps >= 3072 elements (the partial tiles' write, read and reduce are
     // then a small part of the call: the 7B down shape, 3584 × 18944, runs
-    // 7% faster than on 224 unsplit 256 × 128 tiles; q/o, K = 3584, would
-    // run 18% slower).  Only for f16 activations with the f16 cache or a
+    // 7% faster than on 224 unsplit 256 × 128 tiles, 4096 × 14336 at
+    // M = 1024 with ranges of 3584 7%; q/o, K = 3584 in ranges of 1792,
+    // would run 18% slower).  Only for f16 activations with the f16 cache or a
     // fused format other than Q6_K: Q6_K's raw-byte registers, and f32
     // activation registers, do not fit beside 256 accumulators.
     if (!x_f32 && fmt != kFmtQ6_K && M > 128) {
@@ -29,7 +30,7 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
         s = s > k64 / 4 ? k64 / 4 : s;
         const int64_t t128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
         const bool split_fills =
-            t128 < kCUs && s >= 2 && t256 * s >= kCUs * 7 / 8 && K / s >= 4096;
+            t128 < kCUs && s >= 2 && t256 * s >= kCUs * 7 / 8 && K / s >= 3072;
         // More than 3/4 of a round of 256 × 256 tiles also takes them, unsplit:
         // the 256 × 128 grid would be a full round plus a tail of more than
         // 128 tiles, too many to split (14336 × 4096 at M = 1024: 160 -> 139

@@ -228,6 +228,13 @@ def test_workspace_planning(L):
     assert L.mq_gemm_workspace_bytes(12, 300, 32768, 1280, 7) == 5 * 256 * 256 * 256 * 4
     assert L.mq_gemm_workspace_bytes(8, 300, 32768, 1280, 7) == 7 * 256 * 256 * 256 * 4
     assert L.mq_gemm_workspace_bytes(12, 300, 32768, 1280, 3) == 3 * 256 * 256 * 256 * 4
+    # 4096 x 14336 at M = 1024: 64 tiles of 256 x 256 split 4 ways (ranges of
+    # 3584 k fill the compute units); at M = 512 the ranges would be 1792 k, so
+    # the plan keeps 256 x 128 tiles (64 of them, split 4 ways)
+    assert L.mq_gemm_workspace_bytes(0, 1024, 4096, 14336, 0) == 4 * 64 * 256 * 256 * 4
+    assert L.mq_gemm_workspace_bytes(0, 512, 4096, 14336, 0) == 4 * 64 * 256 * 128 * 4
+    # more than 3/4 of a round of 256 x 256 tiles: unsplit, no workspace
+    assert L.mq_gemm_workspace_bytes(0, 1024, 14336, 4096, 0) == 0
     # q/o: 224 tiles of 256 x 128, one partial round that a split cannot double
     assert L.mq_gemm_workspace_bytes(0, 2048, 3584, 3584, 0) == 0
     assert L.mq_gemm_workspace_bytes(0, 64, 512, 512, 1) == 0
