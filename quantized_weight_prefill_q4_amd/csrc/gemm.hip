@@ -19,10 +19,9 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
     // then a small part of the call: the 7B down shape, 3584 × 18944, runs
     // 7% faster than on 224 unsplit 256 × 128 tiles, 4096 × 14336 at
     // M = 1024 with ranges of 3584 7%; q/o, K = 3584 in ranges of 1792,
-    // would run 18% slower).  Only for f16 activations with the f16 cache or a
-    // fused format other than Q6_K: Q6_K's raw-byte registers, and f32
-    // activation registers, do not fit beside 256 accumulators.
-    if (!x_f32 && fmt != kFmtQ6_K && M > 128) {
+    // would run 18% slower).  Only for f16 activations: the f32 activation
+    // registers do not fit beside 256 accumulators.
+    if (!x_f32 && M > 128) {
         const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
         const int k64 = (K + 63) / 64;
         int s = t256 >= kCUs ? 1 : (int)(kCUs / t256);

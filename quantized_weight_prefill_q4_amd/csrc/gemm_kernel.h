@@ -1226,6 +1226,245 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
     store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
 }
 
+// ---------------------------------------------------------------------------
+// Fused Q6_K GEMM on 256 × 256 tiles, expanded in the MFMA operand registers
+// (the layout of gemm_q4k_rb_kernel: 1 × 4 waves, wave w owns weight rows
+// 64w .. 64w + 63 and all 256 activation rows).
+//
+// A Q6_K super-block of a 256-row tile is 53.8 KB, so two of them do not fit
+// in LDS beside the X stages; the unit staged here is a half super-block
+// (128 elements, two k-steps), 8 aligned 16-byte chunks per weight row:
+// chunks 0-3 the half's 64 low-nibble bytes, 4-5 its 32 high-pair bytes, 6
+// the block's 16 scales, 7 the block's last 16 bytes (d in bytes 14-15, so
+// no load reaches past the block's last dword).  The
+// blocks are only 2-byte aligned, so each chunk is loaded as the 20 aligned
+// bytes that contain it and shifted into place (realign16) before its LDS
+// write.  Thread t always stages chunk t mod 8 of rows t / 8 + 32i.  Rows
+// are 9 chunks apart in LDS: at 8 (128 bytes) the 32 rows one lane group
+// reads would share two bank groups; at 144 bytes they spread over 16.
+//
+// Lane l of wave w feeds weight rows 64w + 32f + (l & 31) at k = 16kk +
+// 8(l >> 5) + 0..7 of k-slice kk.  Within quarter c4 = 2h + C2 of the
+// super-block these are elements 128h + 64C2 + 16kk + 8(l >> 5) + 0..7, i.e.
+// group g = 2C2 + kk/2 and position p = 16(kk & 1) + 8(l >> 5) + 0..7: low
+// bits from half bytes 32(kk/2) + p (low nibbles for C2 = 0, high for
+// C2 = 1), high bits from half bytes p of the qh part shifted by 2g, scale
+// 8h + 4C2 + kk.  Value (d·s)·(q − 32) in f32, as the decode (q6k_chunk).
+//
+// Pipeline: X as in gemm_kernel.  Raw weights: two half-super-block buffers;
+// during the two k-steps of half hx the 8 chunks per thread of half hx + 1
+// are loaded (4 per step, one step ahead in a register set) and written to
+// the other buffer, last read in half hx − 1.  K ranges start on even steps.
+// ---------------------------------------------------------------------------
+constexpr int kR6Chunks = 256 * 8;                  // 16-byte chunks of a tile half super-block
+constexpr int kR6Stride = 9;                        // LDS chunks per row
+constexpr int kR6PerThread = kR6Chunks / kThreads;  // 8
+static_assert(kR6PerThread * kThreads == kR6Chunks, "chunks per thread");
+
+// The lane's bytes of one k-step for its two weight rows, and the four
+// factors d·s of its k-slices.
+struct R6Raw {
+    u32x2 ql[2][4], qh[2][2];
+    float ds[2][4];
+};
+
+// h: the half of the super-block the step lies in; C2: its quarter in the half.
+template <int C2>
+__device__ __forceinline__ void r6_fetch(const u32x4 *Bc, int h, int lane, int wave, R6Raw &r) {
+    const int hl = lane >> 5;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * kR6Stride;
+        const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) r.ql[f][kk] = q2[4 * (kk >> 1) + 2 * (kk & 1) + hl];
+        const u32x2 *h2 = reinterpret_cast<const u32x2 *>(blk + 4);
+        r.qh[f][0] = h2[hl];
+        r.qh[f][1] = h2[2 + hl];
+        const uint32_t sw = reinterpret_cast<const uint32_t *>(blk + 6)[2 * h + C2];
+        const float d = f16_bits_to_f32(reinterpret_cast<const uint32_t *>(blk + 7)[3] >> 16);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) r.ds[f][kk] = d * (float)(int)(int8_t)(sw >> (8 * kk));
+    }
+}
+
+template <int C2, int KK>
+__device__ __forceinline__ half8 q6k_frag(const R6Raw &r, int f) {
+    constexpr uint32_t L = 0x0F0F0F0Fu, H = 0x03030303u;
+    constexpr uint32_t n4 = 4 * C2, h2 = 4 * C2 + 2 * (KK >> 1);
+    const u32x2 l = r.ql[f][KK], hb = r.qh[f][KK & 1];
+    const uint32_t q0 = ((l.x >> n4) & L) | (((hb.x >> h2) & H) << 4);
+    const uint32_t q1 = ((l.y >> n4) & L) | (((hb.y >> h2) & H) << 4);
+    return __builtin_bit_cast(half8, q6k_chunk(q0, q1, r.ds[f][KK]));
+}
+
+template <int C2, class Slot>
+__device__ __forceinline__ void rb6_step(const u32x4 *Ac, const u32x4 *Bc, int h,
+                                         f32x16 (&acc)[8][2], int lane, int wave, Slot &&slot) {
+    const int hl = lane >> 5;
+    R6Raw raw;
+    r6_fetch<C2>(Bc, h, lane, wave, raw);
+    half8 af[2][8], bf[2][2];
+    auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
+        constexpr int kk = KKc;
+        const int c = kk * 2 + hl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = i * 32 + (lane & 31);
+            dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
+        }
+    };
+    load_a(std::integral_constant<int, 0>(), af[0]);
+    bf[0][0] = q6k_frag<C2, 0>(raw, 0);
+    bf[0][1] = q6k_frag<C2, 0>(raw, 1);
+    static_for<4>([&](auto KK) MQ_INLINE {
+        constexpr int kk = KK, c = kk & 1;
+        if constexpr (kk + 1 < 4) {
+            load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
+            bf[c ^ 1][0] = q6k_frag<C2, kk + 1>(raw, 0);
+            bf[c ^ 1][1] = q6k_frag<C2, kk + 1>(raw, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<16>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 16 + IJ;
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
+                                                               0);
+            if constexpr (n & 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                slot(std::integral_constant<int, n / 2>());
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    });
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
+    static_assert(FMT == kFmtQ6_K, "Q6_K only");
+    constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
+    constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
+    __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
+    __shared__ u32x4 Bq0[256 * kR6Stride], Bq1[256 * kR6Stride];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = 0, wn = wave;
+    const int pid = blockIdx.x;
+    int tile, part = 0;
+    if (pid < a.dp_tiles) {
+        tile = xcd_remap(pid, a.dp_tiles);
+    } else {
+        const int j = xcd_remap(pid - a.dp_tiles, (int)gridDim.x - a.dp_tiles);
+        const int tt = j % a.tail_tiles;
+        tile = a.dp_tiles + tt;
+        part = j / a.tail_tiles;
+    }
+    const bool tail = pid >= a.dp_tiles;
+    int tm, tn;
+    tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    // K ranges start on even steps and (K a multiple of 256) end on even ones
+    const int kt_begin = tail ? part * a.steps_per_split : 0;
+    const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
+    const int hx_end = kt_end >> 1;
+
+    F16Loader<BM> la;
+    la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
+    constexpr int NA = decltype(la)::NPART;
+    // raw weight chunks: the resource starts at the 16-byte boundary at or
+    // below the tile's first row; chunk p = thread mod 8 of rows r0 + 32i
+    const int rows_valid = min(BN, a.N - n0);
+    const int64_t start = (int64_t)n0 * a.ldw;
+    const uint32_t shift0 = (uint32_t)(((uintptr_t)a.W + start) & 15);
+    const int64_t extent = shift0 + (int64_t)rows_valid * a.ldw;
+    const __amdgpu_buffer_rsrc_t rsb =
+        make_rsrc(a.W + start - shift0, (uint32_t)((extent + 3) & ~(int64_t)3));
+    const int p = (int)threadIdx.x & 7, r0 = (int)threadIdx.x >> 3;
+    const uint32_t psrc0 = p < 4 ? 16u * p : (p < 6 ? 128u + 16u * (p - 4) : (p == 6 ? 192u : 194u));
+    const uint32_t phalf = p < 4 ? 64u : (p < 6 ? 32u : 0u);   // + phalf·h for half h
+    uint32_t roff[kR6PerThread];
+#pragma unroll
+    for (int i = 0; i < kR6PerThread; ++i) roff[i] = shift0 + (uint32_t)((r0 + 32 * i) * a.ldw) + psrc0;
+    uint32_t bv[2][4][5], bsh[2][4];
+    // load chunk i of half hx into slot (set, j)
+    auto bload = [&](int set, int j, int i, int hx) MQ_INLINE {
+        const uint32_t o = hx < hx_end ? roff[i] + (uint32_t)(hx >> 1) * 210u + phalf * (hx & 1)
+                                       : kOOB;
+        bsh[set][j] = o & 2;
+        load5(rsb, o, bv[set][j]);
+    };
+    auto bstore = [&](int set, int j, int i, u32x4 *buf) MQ_INLINE {
+        buf[(r0 + 32 * i) * kR6Stride + p] = realign16(bv[set][j], bsh[set][j]);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    // prologue: half kt_begin / 2 whole in its buffer, X step kt_begin in
+    // stage 0, X step kt_begin + 1 and part 0 of the next half in set 1
+    {
+        const int hx0 = kt_begin >> 1, k0 = kt_begin * BK;
+        u32x4 *B = (hx0 & 1) ? Bq1 : Bq0;
+        la.begin(0, k0, true);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.load(0, i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bload(0, i, i, hx0);
+        la.begin(1, k0 + BK, kt_begin + 1 < kt_end);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.load(1, i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bstore(0, i, i, B);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bload(0, i, 4 + i, hx0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bload(1, i, i, hx0 + 1);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.store(0, i, A0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bstore(0, i, 4 + i, B);
+        sync_lds();
+    }
+
+    // Step kt (C2 = kt & 1 = P): slots 0..15 load part 1 − C2 of the half
+    // that step kt + 1 writes (half kt/2 + 1 for C2 = 0, kt/2 + 2 for C2 = 1)
+    // into set P; slots 16..31 write set 1 − P (part C2 of half kt/2 + 1).
+    auto step = [&](auto C2c, int kt) MQ_INLINE {
+        constexpr int C2 = decltype(C2c)::value, P = C2;
+        constexpr int H = 16, NB = 4;
+        u32x4 *An = P ? A0 : A1;
+        const int hx = kt >> 1;
+        const u32x4 *Bc = (hx & 1) ? Bq1 : Bq0;
+        u32x4 *Bn = (hx & 1) ? Bq0 : Bq1;
+        const int hl_next = C2 == 0 ? hx + 1 : hx + 2;
+        constexpr int lpart = 1 - C2;
+        la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
+        rb6_step<C2>(P ? A1 : A0, Bc, hx & 1, acc, lane, wave, [&](auto SL) MQ_INLINE {
+            constexpr int sl = SL, half = sl < H ? sl : sl - H;
+            constexpr int TOT = NA + NB;
+            constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
+            static_for<hi - lo>([&](auto O) MQ_INLINE {
+                constexpr int o = lo + O;
+                if constexpr (sl < H) {
+                    if constexpr (o < NA) la.load(P, o);
+                    else bload(P, o - NA, 4 * lpart + (o - NA), hl_next);
+                } else {
+                    if constexpr (o < NA) la.store(1 - P, o, An);
+                    else bstore(1 - P, o - NA, 4 * C2 + (o - NA), Bn);
+                }
+            });
+        });
+        sync_lds();
+    };
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
+        step(std::integral_constant<int, 0>(), kt);
+        step(std::integral_constant<int, 1>(), kt + 1);
+    }
+    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+}
+
 // Y tile = Σ_s partial[s] in the order s = 0, 1, ..., split − 1, for every
 // tail tile.  Block (tail tile, chunk) handles 1024 consecutive elements of
 // the BM × BN partial tile, four per thread.
@@ -1272,7 +1511,10 @@ hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t strea
         if constexpr (FMT == kFmtQ4_K && !XF32) {
             hipLaunchKernelGGL(gemm_q4k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
             return hipGetLastError();
-        } else if constexpr (FMT != kFmtQ6_K && !XF32) {
+        } else if constexpr (FMT == kFmtQ6_K && !XF32) {
+            hipLaunchKernelGGL(gemm_q6k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
+            return hipGetLastError();
+        } else if constexpr (!XF32) {
             return launch_tile<256, 256, FMT, XF32>(a, grid, stream);
         }
     } else if (bm == 256 && bn == 128) {

@@ -215,12 +215,9 @@ def test_workspace_planning(L):
     # gate/up: 8 x 74 tiles of 256 x 256 = two full rounds of 256 plus 80 tiles,
     # which are split 256 // 80 = 3 ways along K
     assert L.mq_gemm_workspace_bytes(0, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
-    # the Q4_K fused kernel uses the same tiles (same plan); Q6_K keeps 256 x 128
-    # tiles: 4 rounds + 160 tiles -> no split
-    assert L.mq_gemm_workspace_bytes(12, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
-    assert L.mq_gemm_workspace_bytes(14, 2048, 18944, 3584, 0) == 0
-    # every other weight format takes the 256 x 256 fused tiles too
-    for fmt in (2, 6, 7, 8, 13):
+    # every fused weight format takes the same 256 x 256 tiles (same plan);
+    # Q6_K's 3-way split of 56 steps is 20, 20, 16 (ranges start even)
+    for fmt in (2, 6, 7, 8, 12, 13, 14):
         assert L.mq_gemm_workspace_bytes(fmt, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
     # the Q4_K 256 x 256 kernel stages whole super-blocks: its K ranges are
     # multiples of 4 k-steps, so a requested 7-way split of 20 steps becomes
@@ -245,9 +242,8 @@ def test_workspace_planning(L):
     # (2048 rows of 3584 halves, already a multiple of 256 bytes), then the
     # f16-activation plan with its split planes behind it
     x16 = 2048 * 3584 * 2
-    for fmt in (0, 2, 12, 13):
+    for fmt in (0, 2, 12, 13, 14):
         assert L.mq_gemm_xf32_workspace_bytes(fmt, 2048, 18944, 3584, 0) == x16 + 3 * 80 * 256 * 256 * 4
-    assert L.mq_gemm_xf32_workspace_bytes(14, 2048, 18944, 3584, 0) == x16
     assert L.mq_gemm_xf32_workspace_bytes(12, 2048, 512, 3584, 0) == x16 + ws
     # padded row stride for the converted X when 2K bytes is a multiple of 2048;
     # 65 rows of 4160 halves = 540800 bytes, rounded up to 540928

@@ -86,6 +86,31 @@ def test_q4k_large_tile_k_ranges_exact(M, N, K, split):
     assert np.array_equal(Y[rows].astype(np.float64), Yref)
 
 
+@pytest.mark.parametrize("M,N,K,split", [(2011, 8348, 2048, 0), (2011, 8348, 2048, 3),
+                                         (2048, 3584, 8192, 0), (1000, 14336, 768, 0),
+                                         (300, 32768, 768, 5)])
+def test_q6k_large_tile_k_ranges_exact(M, N, K, split):
+    """The Q6_K 256 x 256 kernel stages half super-blocks (2 k-steps) whose
+    bytes it re-aligns from 2-byte-aligned blocks: ragged M and N, a forced
+    3-way split of 32 steps (ranges 12, 12, 8), the down-like split of 128
+    steps in 2 ranges of 64, and with K = 768 (630-byte rows, so row starts
+    fall on every even residue mod 16) a 3/4 round unsplit and a 5-way split
+    of 12 steps (ranges of 4, 4, 4) with the second M-tile 44 rows deep.  Integer inputs: every sampled
+    element exact, and equal to the cache path at split 1."""
+    q = synth.weights(14, synth.rng(36, 0, 14, N), N, K, mode="integer")
+    x = synth.activations(synth.rng(36, role=1), M, K, mode="integer")
+    Y = to_host(_fused(14, x, q, N, K, split_k=split))
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(36).choice(M, 12)]))
+    w16 = oracle.dequant_ref(14, q, N, K)
+    Yref, _ = oracle.gemm_ref(x[rows], w16)
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
+    if split == 0:
+        Yf1 = to_host(_fused(14, x, q, N, K, split_k=1))
+        announce("gemm_f16cache", "Q6_K cache", f"M={M} N={N} K={K}", "split=1")
+        Yc1 = to_host(mq.gemm_f16cache(to_dev_f16(x), to_dev_f16(w16), K, split_k=1))
+        assert np.array_equal(Yf1, Yc1)
+
+
 @pytest.mark.parametrize("fmt,M,N,K", [(12, 64, 512, 512), (12, 129, 200, 1280),
                                        (14, 257, 96, 768), (8, 65, 333, 4128),
                                        (8, 1, 1, 32), (14, 1, 3, 256)])
