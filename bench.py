@@ -79,6 +79,8 @@ def parse():
                    help="layers (7 matrices each) of the oracle sample")
     p.add_argument("--only-shape", default=None,
                    help="profiling aid: run only this 7B matrix's cache GEMM --steps times")
+    p.add_argument("--only-fused", default=None,
+                   help="profiling aid: run only this 7B matrix's fused GEMM --steps times")
     p.add_argument("--only-mmq", default=None,
                    help="time only this 7B shape on the int8 path (for counter runs)")
     p.add_argument("--only-load", action="store_true",
@@ -143,6 +145,26 @@ def run_only_shape(torch, mq, name, steps, dev):
                       "median_call_us": round(us, 2),
                       "tflops": round(2.0 * M * N * K / us / 1e6, 1),
                       "algorithmic_bytes_per_call": M * K * 2 + N * K * 2 + M * N * 4}), flush=True)
+
+
+def run_only_fused(torch, mq, name, steps, dev):
+    fmt, N, K = next((f, n, k) for nm, f, n, k in synth.LAYER_7B if nm == name)
+    M = 2048
+    q = synth.weights_device(fmt, 1, N, K, dev)
+    x = synth.activations_device(2, M, K, dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, mq.workspace_bytes(fmt, M, N, K) // 4), dtype=torch.float32, device=dev)
+    mq.gemm_fused(x, q, fmt, N, K, out=y, ws=ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record()
+        mq.gemm_fused(x, q, fmt, N, K, out=y, ws=ws)
+    ev[steps].record()
+    torch.cuda.synchronize()
+    us = statistics.median(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+    print(json.dumps({"only_fused": name, "format": fmt, "M": M, "N": N, "K": K,
+                      "calls": steps + 1, "median_call_us": round(us, 2),
+                      "tflops": round(2.0 * M * N * K / us / 1e6, 1)}), flush=True)
 
 
 def run_only_mmq(torch, mq, name, steps, dev):
@@ -713,6 +735,9 @@ def main():
         return
     if args.only_shape:
         run_only_shape(torch, mq, args.only_shape, args.steps, dev)
+        return
+    if args.only_fused:
+        run_only_fused(torch, mq, args.only_fused, args.steps, dev)
         return
     if args.only_mmq:
         run_only_mmq(torch, mq, args.only_mmq, args.steps, dev)
