@@ -516,6 +516,35 @@ def mmq_forward(torch, mq, W, M, steps, dev):
     return statistics.median(d), qms
 
 
+def vendor_table(torch, W, xa, xf, shape_us, reps=20):
+    """The same 7B products through the vendor library (torch.mm, hipBLASLt:
+    f16 inputs, f16 output, f32 accumulation) on layer 0's decoded caches,
+    median of `reps` calls, next to this library's per-call medians from the
+    instrumented forward (f32 output).  Context only: the library writes half
+    the output bytes."""
+    out = {}
+    for name in ("q", "k", "gate", "down"):
+        fmt, N, K, q, cache = W[0][name]
+        x = xf if name == "down" else xa
+        wt = cache[:, :K].t().contiguous()          # [K, N]: a plain NN product
+        torch.mm(x, wt)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for i in range(reps):
+            evs[i].record()
+            torch.mm(x, wt)
+        evs[reps].record()
+        torch.cuda.synchronize()
+        us = statistics.median(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(reps))
+        M = x.shape[0]
+        out[name] = {"N": N, "K": K, "vendor_us": round(us, 2),
+                     "vendor_tflops": round(2.0 * M * N * K / us / 1e6, 1),
+                     "ours_us": round(shape_us[name], 2),
+                     "ours_tflops": round(2.0 * M * N * K / shape_us[name] / 1e6, 1)}
+        del wt
+    torch.cuda.empty_cache()
+    return out
+
+
 def grouped_forward(torch, mq, W, xa, xf, steps, dev):
     """The forward with the shared-input GEMMs grouped: per layer one q|k|v GEMM
     (N = 4608), o, one gate|up GEMM (N = 37888) and down — 112 calls instead of
@@ -862,6 +891,11 @@ def main():
         log(f"[bench] dense f16 peak at the roofline kernel's clock {at:.0f} TFLOP/s; "
             f"the kernel reaches {100 * ach / at:.1f}% of it")
 
+    # -- the vendor library on the same shapes (context) --------------------------------
+    vendor = vendor_table(torch, W, xa, xf, {n: t for n, _, _, t, _ in shape_rows})
+    log("[bench] vendor library (torch.mm / hipBLASLt, f16 out) vs this library (f32 out), M = 2048: " +
+        ", ".join(f"{n} {v['vendor_us']:.1f} vs {v['ours_us']:.1f} us" for n, v in vendor.items()))
+
     # -- grouped shared-input forward (q|k|v and gate|up as one GEMM each) ------------
     grouped = None
     if args.grouped_steps > 0:
@@ -981,6 +1015,7 @@ def main():
         "fused": fused,
         "mmq_forward": mmqf,
         "grouped_forward": grouped,
+        "vendor_gemm": vendor,
         "crossover": cross,
         "formats": fmts,
         "xf32": xf32,
