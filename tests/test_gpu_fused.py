@@ -111,6 +111,33 @@ def test_q6k_large_tile_k_ranges_exact(M, N, K, split):
         assert np.array_equal(Yf1, Yc1)
 
 
+def _large_tile_cases(seed, n):
+    """Seeded shapes that take the 256 x 256 register-expansion kernels: more
+    than 3/4 of a round of tiles (so N >= 48 · 256 / ceil(M / 256)), ragged M
+    and N, K a multiple of 256, and a random forced split (0 = the plan's)."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        tm = int(g.integers(1, 9))
+        M = 256 * tm - int(g.integers(0, 200)) if tm > 1 else int(g.integers(129, 257))
+        tn = -(-193 // tm) + int(g.integers(0, 8))
+        N = 256 * tn - int(g.integers(0, 256))
+        K = 256 * int(g.integers(1, 7))
+        out.append((M, N, K, int(g.choice([0, 0, 2, 3, 5]))))
+    return out
+
+
+@pytest.mark.parametrize("fmt", [12, 14])
+@pytest.mark.parametrize("M,N,K,split", _large_tile_cases(37, 4))
+def test_register_expansion_kernels_random_shapes_exact(fmt, M, N, K, split):
+    q = synth.weights(fmt, synth.rng(37, 0, fmt, N + K), N, K, mode="integer")
+    x = synth.activations(synth.rng(37, role=1), M, K, mode="integer")
+    Y = to_host(_fused(fmt, x, q, N, K, split_k=split))
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(M, 8)]))
+    Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(fmt, q, N, K))
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
+
+
 @pytest.mark.parametrize("fmt,M,N,K", [(12, 64, 512, 512), (12, 129, 200, 1280),
                                        (14, 257, 96, 768), (8, 65, 333, 4128),
                                        (8, 1, 1, 32), (14, 1, 3, 256)])
