@@ -32,9 +32,10 @@
 // aligned dwords re-assembled with v_alignbyte), expand them to f16 in
 // registers with the decode arithmetic of the standalone dequant kernel, and
 // store the f16 tile to LDS: each weight element is expanded once per block
-// tile (⌈M/BM⌉ times in all), not once per wave.  Fused Q4_K on 256 × 256
-// tiles has a kernel of its own (gemm_q4k_rb_kernel, below) that stages raw
-// super-blocks in LDS and expands them in the MFMA operand registers.
+// tile (⌈M/BM⌉ times in all), not once per wave.  Fused Q4_K and Q6_K on
+// 256 × 256 tiles have kernels of their own (gemm_q4k_rb_kernel,
+// gemm_q6k_rb_kernel, below) that stage raw (half) super-blocks in LDS and
+// expand them in the MFMA operand registers.
 
 #pragma once
 
