@@ -154,6 +154,29 @@ def test_random_tolerance_and_cache_identity(fmt, M, N, K):
     assert np.array_equal(Yf1, Yc1), f"fused and cache paths differ: max {np.abs(Yf1 - Yc1).max()}"
 
 
+SHAPES_7B = [("q/o", 12, 3584, 3584), ("k/v", 12, 512, 3584), ("gate/up", 12, 18944, 3584),
+             ("down", 14, 3584, 18944)]
+
+
+@pytest.mark.parametrize("name,fmt,N,K", SHAPES_7B)
+def test_7b_shapes_m2048_random(name, fmt, N, K):
+    """The fused forward's products at full size, random data: sampled rows
+    within tolerance under the plan the bench times, and the whole output
+    equal to the cache GEMM's when neither splits K."""
+    M = 2048
+    q = synth.weights(fmt, synth.rng(38, 0, fmt, N % 1000), N, K)
+    x = synth.activations(synth.rng(38, role=1), M, K)
+    Y = to_host(_fused(fmt, x, q, N, K))
+    w16 = oracle.dequant_ref(fmt, q, N, K)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(N).choice(M, 12)]))
+    check_gemm(Y[rows], x, w16, K, f"fused 7B {name}", rows=rows)
+    assert np.all(np.isfinite(Y))
+    Yf1 = to_host(_fused(fmt, x, q, N, K, split_k=1))
+    announce("gemm_f16cache", name, f"M={M} N={N} K={K}", "split=1")
+    Yc1 = to_host(mq.gemm_f16cache(to_dev_f16(x), to_dev_f16(w16), K, split_k=1))
+    assert np.array_equal(Yf1, Yc1)
+
+
 SWEEP = [("Q4_K 4096^2", 12, 4096, 4096), ("Q4_K 14336x4096", 12, 14336, 4096),
          ("Q4_K 4096x14336", 12, 4096, 14336), ("Q8_0 4096^2", 8, 4096, 4096),
          ("Q6_K 3584x18944", 14, 3584, 18944)]
