@@ -42,6 +42,30 @@ def _row_major_2d(t: torch.Tensor, name: str) -> int:
     return t.stride(0)
 
 
+# The C ABI sees plain pointers; the sizes it cannot check are checked here,
+# so that a wrong argument is an exception rather than an access out of bounds.
+def _need_shape(t: torch.Tensor, rows: int, cols: int, name: str) -> None:
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} must be at least {rows} x {cols}, got {tuple(t.shape)}")
+
+
+def _need_span(t: torch.Tensor, elems: int, name: str) -> None:
+    """t's storage holds `elems` elements from t's first one (rows written at
+    the full row stride, e.g. a cache's pad columns)."""
+    have = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if have < elems:
+        raise ValueError(f"{name} spans {have} elements, {elems} needed")
+
+
+def _need_quant(wq: torch.Tensor, f: int, N: int, K: int) -> None:
+    _need_cuda(wq, "wq", torch.uint8)
+    if not wq.is_contiguous():
+        raise ValueError("wq must be contiguous")
+    need = N * check(lib().mq_row_bytes(f, K), "mq_row_bytes")
+    if wq.numel() < need:
+        raise ValueError(f"wq holds {wq.numel()} bytes; {N} rows of K = {K} need {need}")
+
+
 def block_elems(fmt) -> int:
     return check(lib().mq_block_elems(_fmt(fmt)), "mq_block_elems")
 
@@ -71,15 +95,15 @@ def dequant_to_f16(wq: torch.Tensor, fmt, N: int, K: int, pad: bool = True,
     """Decode a quantized N×K weight (uint8, rows contiguous) into an f16 cache
     [N, ld]; ld = cache_ld(K) when pad else K.  Use ``[:, :K]`` for the matrix."""
     f = _fmt(fmt)
-    _need_cuda(wq, "wq", torch.uint8)
-    if not wq.is_contiguous():
-        raise ValueError("wq must be contiguous")
+    _need_quant(wq, f, N, K)
     ld = cache_ld(K) if pad else K
     if out is None:
         out = torch.empty((N, ld), dtype=torch.float16, device=wq.device)
     else:
         _need_cuda(out, "out", torch.float16)
         ld = _row_major_2d(out, "out")
+        _need_shape(out, N, K, "out")
+        _need_span(out, N * ld, "out")
     check(lib().mq_dequant_to_f16(f, wq.data_ptr(), N, K, out.data_ptr(), ld, _stream(wq)),
           "mq_dequant_to_f16")
     return out
@@ -96,15 +120,15 @@ def dequant_to_f16_batch(jobs, pad: bool = True) -> list[torch.Tensor]:
     for i, job in enumerate(jobs):
         wq, fmt, N, K = job[:4]
         out = job[4] if len(job) > 4 else None
-        _need_cuda(wq, "wq", torch.uint8)
-        if not wq.is_contiguous():
-            raise ValueError("wq must be contiguous")
+        _need_quant(wq, _fmt(fmt), N, K)
         ld = cache_ld(K) if pad else K
         if out is None:
             out = torch.empty((N, ld), dtype=torch.float16, device=wq.device)
         else:
             _need_cuda(out, "out", torch.float16)
             ld = _row_major_2d(out, "out")
+            _need_shape(out, N, K, "out")
+            _need_span(out, N * ld, "out")
         if stream is None:
             stream = _stream(wq)
         arr[i] = MqDequantJob(_fmt(fmt), N, K, ld, wq.data_ptr(), out.data_ptr())
@@ -140,11 +164,14 @@ def gemm_f16cache(x: torch.Tensor, w16: torch.Tensor, K: int | None = None, spli
     ldw = _row_major_2d(w16, "w16")
     M, N = x.shape[0], w16.shape[0]
     K = x.shape[1] if K is None else K
+    _need_shape(x, M, K, "x")
+    _need_shape(w16, N, K, "w16")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     else:
         _need_cuda(out, "out", torch.float32)
     ldy = _row_major_2d(out, "out")
+    _need_shape(out, M, N, "out")
     if ws is None:
         ws = _workspace(0, M, N, K, split_k, x.device, xf32)
     fn = "mq_gemm_f16cache_xf32" if xf32 else "mq_gemm_f16cache"
@@ -162,17 +189,17 @@ def gemm_fused(x: torch.Tensor, wq: torch.Tensor, fmt, N: int, K: int | None = N
     in-kernel; x f16, or f32 rounded to f16 inside the kernel."""
     f = _fmt(fmt)
     xf32 = _x_kind(x)
-    _need_cuda(wq, "wq", torch.uint8)
-    if not wq.is_contiguous():
-        raise ValueError("wq must be contiguous")
     ldx = _row_major_2d(x, "x")
     M = x.shape[0]
     K = x.shape[1] if K is None else K
+    _need_shape(x, M, K, "x")
+    _need_quant(wq, f, N, K)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     else:
         _need_cuda(out, "out", torch.float32)
     ldy = _row_major_2d(out, "out")
+    _need_shape(out, M, N, "out")
     if ws is None:
         ws = _workspace(f, M, N, K, split_k, x.device, xf32)
     fn = "mq_gemm_fused_xf32" if xf32 else "mq_gemm_fused"
@@ -190,11 +217,13 @@ def convert_f32_to_f16(x: torch.Tensor, K: int | None = None,
     ldx = _row_major_2d(x, "x")
     M = x.shape[0]
     K = x.shape[1] if K is None else K
+    _need_shape(x, M, K, "x")
     if out is None:
         out = torch.empty((M, K), dtype=torch.float16, device=x.device)
     else:
         _need_cuda(out, "out", torch.float16)
     ld16 = _row_major_2d(out, "out")
+    _need_shape(out, M, K, "out")
     check(lib().mq_convert_f32_to_f16(x.data_ptr(), ldx, out.data_ptr(), ld16, M, K, _stream(x)),
           "mq_convert_f32_to_f16")
     return out
@@ -208,11 +237,13 @@ def quantize_q8_1(x: torch.Tensor, K: int | None = None, xq: torch.Tensor | None
     ldx = _row_major_2d(x, "x")
     M = x.shape[0]
     K = x.shape[1] if K is None else K
+    _need_shape(x, M, K, "x")
     if xq is None:
         xq = torch.empty((M, (K + 15) // 16 * 16), dtype=torch.int8, device=x.device)
     else:
         _need_cuda(xq, "xq", torch.int8)
     ldq = _row_major_2d(xq, "xq")
+    _need_shape(xq, M, K, "xq")
     if ds is None:
         ds = torch.empty((M, K // 32, 2), dtype=torch.float32, device=x.device)
     else:
@@ -237,16 +268,20 @@ def gemm_mmq(xq: torch.Tensor, ds: torch.Tensor, wq: torch.Tensor, fmt, N: int, 
     f = _fmt(fmt)
     _need_cuda(xq, "xq", torch.int8)
     _need_cuda(ds, "ds", torch.float32)
-    _need_cuda(wq, "wq", torch.uint8)
-    if not wq.is_contiguous() or not ds.is_contiguous():
-        raise ValueError("wq and ds must be contiguous")
+    _need_quant(wq, f, N, K)
+    if not ds.is_contiguous():
+        raise ValueError("ds must be contiguous")
     ldq = _row_major_2d(xq, "xq")
     M = xq.shape[0]
+    _need_shape(xq, M, K, "xq")
+    if ds.numel() < M * (K // 32) * 2:
+        raise ValueError(f"ds holds {ds.numel()} floats; {M * (K // 32) * 2} needed")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
     else:
         _need_cuda(out, "out", torch.float32)
     ldy = _row_major_2d(out, "out")
+    _need_shape(out, M, N, "out")
     if ws is None:
         nbytes = mmq_workspace_bytes(f, M, N, K, split_k)
         ws = torch.empty(nbytes // 4, dtype=torch.float32, device=xq.device) if nbytes else None
