@@ -46,6 +46,7 @@ ROOFLINE_KERNEL = "gemm_kernel<256, 256, f16> + splitk_reduce (mq_gemm_f16cache,
 # on; reported only while the source is unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_f16cache_gate_7b_m2048_traffic.md")
 GEMM_SOURCES = ("quantized_weight_prefill_q4_amd/csrc/gemm_kernel.h",
+                "quantized_weight_prefill_q4_amd/csrc/gemm_fused_rb.h",
                 "quantized_weight_prefill_q4_amd/csrc/gemm.hip",
                 "quantized_weight_prefill_q4_amd/csrc/mq_device.h")
 

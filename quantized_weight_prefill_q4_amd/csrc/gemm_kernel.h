@@ -932,539 +932,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
 }
 
-// ---------------------------------------------------------------------------
-// Fused Q4_K GEMM on 256 × 256 tiles with the weights expanded straight into
-// the MFMA operand registers.
-//
-// In gemm_kernel the fused loaders expand a k-step's B tile once per
-// workgroup and write it to LDS as f16 (32 KB), which the 2×2 waves then read
-// back (64 KB per k-step).  Here the 4 waves are laid out 1 × 4: wave w owns
-// weight rows 64w .. 64w + 63 of the tile and all 256 activation rows, so
-// each weight element is still expanded exactly once per tile, by the lane
-// that feeds it to the MFMA.  The raw super-blocks (144 bytes per weight row)
-// are staged in LDS a whole 256-element super-block at a time — the tile's
-// 256 rows × 144 contiguous bytes, each 16-byte chunk loaded once, so the
-// global loads stay whole cache lines — and each lane reads the 16 quant
-// bytes and the header of its rows per k-step.  B then costs 9 KB of LDS
-// writes and 16 KB of reads per k-step instead of 32 + 64 KB, while the X
-// fragment reads double (every wave reads all 256 rows: 128 KB); the global
-// bytes are the same.  Measured on the 7B gate shape against the 2×2 fused
-// kernel: texture-address stalls −90%, LDS bank conflicts −70%, 2-4% less
-// time; the expansion's VALU work (~2.8 instructions per element) is what
-// remains between this kernel and the f16-cache GEMM.
-//
-// Lane l of wave w feeds weight rows 64w + 32f + (l & 31) (f = 0, 1) at
-// k = 16kk + 8(l >> 5) + 0..7 of k-slice kk, which are, within the k-step's
-// 64-element quarter c4 of the super-block, the low nibbles of quant bytes
-// 32c4 + 8(l >> 5) + 0..7 (kk = 0) and 32c4 + 16 + 8(l >> 5) + 0..7 (kk = 1)
-// with sub-block 2c4's scale and min, and the high nibbles of the same bytes
-// (kk = 2, 3) with sub-block 2c4 + 1's.  The arithmetic is the decode's
-// (q4k_chunk), so the expanded values are the cache's bit for bit, and the
-// MFMAs see the same operands in the same order as the cache kernel's.
-//
-// Pipeline: X as in gemm_kernel (two register sets, two LDS stages, loads
-// two k-steps ahead).  Raw weights: two super-block buffers; during the four
-// k-steps of super-block sb the 2304 chunks of super-block sb + 1 are loaded
-// (9 per thread: 3 in each of the first three steps, one step ahead in a
-// register set) and written to the other buffer, which is not read before
-// the last quarter of super-block sb.  Each k-step reads the next step's raw
-// bytes and expands its first k-slice between its own MFMAs; for the last
-// quarter that is the next super-block, complete since the third quarter's
-// barrier (the fourth quarter writes no part).  K ranges are whole
-// super-blocks.
-// ---------------------------------------------------------------------------
-constexpr int kRbChunks = 256 * 144 / 16;           // 16-byte chunks of a tile super-block
-constexpr int kRbPerThread = kRbChunks / kThreads;  // 9
-static_assert(kRbPerThread * kThreads == kRbChunks, "chunks per thread");
+}  // namespace
+}  // namespace mq
 
-// Chunks [lo, hi) of the thread's 9 belong to part c4 (loaded for step c4).
-template <int C4>
-struct RbPart {
-    static constexpr int lo = C4 * 3 < kRbPerThread ? C4 * 3 : kRbPerThread;
-    static constexpr int hi = (C4 + 1) * 3 < kRbPerThread ? (C4 + 1) * 3 : kRbPerThread;
-};
+#include "gemm_fused_rb.h"
 
-// Scale and min (as the f32 factors d·sc and dmin·m) of sub-blocks 2c4 and
-// 2c4 + 1 from a super-block header (d, dmin, 12 scale bytes).
-template <int C4>
-__device__ __forceinline__ void q4k_sub_scales(const u32x4 h, float &A0, float &C0, float &A1,
-                                               float &C1) {
-    uint32_t sc0, m0, sc1, m1;
-    if constexpr (C4 < 2) {
-        constexpr int s0 = 16 * C4, s1 = s0 + 8;
-        sc0 = (h.y >> s0) & 63;
-        m0 = (h.z >> s0) & 63;
-        sc1 = (h.y >> s1) & 63;
-        m1 = (h.z >> s1) & 63;
-    } else {
-        constexpr int s0 = 16 * (C4 - 2), s1 = s0 + 8;
-        sc0 = ((h.w >> s0) & 15) | (((h.y >> (s0 + 6)) & 3) << 4);
-        m0 = ((h.w >> (s0 + 4)) & 15) | (((h.z >> (s0 + 6)) & 3) << 4);
-        sc1 = ((h.w >> s1) & 15) | (((h.y >> (s1 + 6)) & 3) << 4);
-        m1 = ((h.w >> (s1 + 4)) & 15) | (((h.z >> (s1 + 6)) & 3) << 4);
-    }
-    const float d = f16_bits_to_f32(h.x), dmin = f16_bits_to_f32(h.x >> 16);
-    A0 = d * (float)sc0;
-    C0 = dmin * (float)m0;
-    A1 = d * (float)sc1;
-    C1 = dmin * (float)m1;
-}
-
-// The B fragment of k-slice kk from the lane's quant bytes qa (bytes 8h..)
-// and qb (bytes 16 + 8h..) of the quarter.
-template <int KK>
-__device__ __forceinline__ half8 q4k_frag(u32x2 qa, u32x2 qb, float A0, float C0, float A1,
-                                          float C1) {
-    constexpr uint32_t L = 0x0F0F0F0Fu;
-    const u32x2 q = (KK & 1) ? qb : qa;
-    const uint32_t w0 = (KK < 2) ? (q.x & L) : ((q.x >> 4) & L);
-    const uint32_t w1 = (KK < 2) ? (q.y & L) : ((q.y >> 4) & L);
-    return __builtin_bit_cast(half8, q4k_chunk(w0, w1, KK < 2 ? A0 : A1, KK < 2 ? C0 : C1));
-}
-
-// What a lane needs of its two weight rows for one k-step: the quant bytes
-// (qa: bytes 8h.., qb: bytes 16 + 8h.. of the quarter), the two sub-blocks'
-// factors, and the expanded fragments of k-slice 0.  Read and computed during
-// the previous k-step, so a step starts with its first MFMAs.
-struct RbRaw {
-    u32x2 qa[2], qb[2];
-    float A0[2], C0[2], A1[2], C1[2];
-    half8 bf0[2];
-};
-
-template <int C4>
-__device__ __forceinline__ void rb_fetch(const u32x4 *Bc, int lane, int wave, RbRaw &r) {
-    const int h = lane >> 5;
-    u32x4 hdr[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * 9;   // the row's 144 bytes
-        hdr[f] = blk[0];
-        const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk + 1 + 2 * C4);
-        r.qa[f] = q2[h];
-        r.qb[f] = q2[2 + h];
-    }
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        q4k_sub_scales<C4>(hdr[f], r.A0[f], r.C0[f], r.A1[f], r.C1[f]);
-        r.bf0[f] = q4k_frag<0>(r.qa[f], r.qb[f], r.A0[f], r.C0[f], r.A1[f], r.C1[f]);
-    }
-}
-
-// One k-step of the wave's 256 × 64 tile from X stage Ac and the raw bytes
-// `cur` (fetched during the previous step); fetches the next step's raw
-// bytes (quarter NC4 of buffer Bnext) into `nxt` between the MFMAs.
-template <int NC4, class Slot>
-__device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32x16 (&acc)[8][2],
-                                        int lane, int wave, const RbRaw &cur, RbRaw &nxt,
-                                        Slot &&slot) {
-    const int h = lane >> 5;
-    half8 af[2][8], bf[2][2];
-    auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
-        constexpr int kk = KKc;
-        const int c = kk * 2 + h;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = i * 32 + (lane & 31);
-            dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
-        }
-    };
-    load_a(std::integral_constant<int, 0>(), af[0]);
-    bf[0][0] = cur.bf0[0];
-    bf[0][1] = cur.bf0[1];
-    static_for<4>([&](auto KK) MQ_INLINE {
-        constexpr int kk = KK, c = kk & 1;
-        if constexpr (kk + 1 < 4) {
-            load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-                bf[c ^ 1][f] = q4k_frag<kk + 1>(cur.qa[f], cur.qb[f], cur.A0[f], cur.C0[f],
-                                                cur.A1[f], cur.C1[f]);
-        } else {
-            rb_fetch<NC4>(Bnext, lane, wave, nxt);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<16>([&](auto IJ) MQ_INLINE {
-            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 16 + IJ;
-            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
-                                                               0);
-            if constexpr (n & 1) {
-                __builtin_amdgcn_sched_barrier(0);
-                slot(std::integral_constant<int, n / 2>());
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        });
-    });
-}
-
-template <int FMT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
-    static_assert(FMT == kFmtQ4_K, "Q4_K only");
-    constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
-    constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
-    __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
-    __shared__ u32x4 Bq0[kRbChunks], Bq1[kRbChunks];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = 0, wn = wave;
-    const int pid = blockIdx.x;
-    int tile, part = 0;
-    if (pid < a.dp_tiles) {
-        tile = xcd_remap(pid, a.dp_tiles);
-    } else {
-        const int j = xcd_remap(pid - a.dp_tiles, (int)gridDim.x - a.dp_tiles);
-        const int tt = j % a.tail_tiles;
-        tile = a.dp_tiles + tt;
-        part = j / a.tail_tiles;
-    }
-    const bool tail = pid >= a.dp_tiles;
-    int tm, tn;
-    tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    // K ranges are whole super-blocks (the plan's steps_per_split is a
-    // multiple of 4, and K of 256)
-    const int kt_begin = tail ? part * a.steps_per_split : 0;
-    const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
-    const int sb_end = kt_end >> 2;
-
-    F16Loader<BM> la;
-    la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
-    constexpr int NA = decltype(la)::NPART;
-    // raw weight chunks: chunk c = thread + 256·i is byte 16(c mod 9) of the
-    // super-block of tile row c / 9, and lands at LDS chunk c
-    const int rows_valid = min(BN, a.N - n0);
-    const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(a.W + (int64_t)n0 * a.ldw, (uint32_t)(rows_valid * a.ldw));
-    uint32_t goff[kRbPerThread];
-#pragma unroll
-    for (int i = 0; i < kRbPerThread; ++i) {
-        const int c = (int)threadIdx.x + kThreads * i, r = c / 9;
-        goff[i] = (uint32_t)(r * a.ldw + 16 * (c - 9 * r));
-    }
-    u32x4 bv[2][3];
-    RbRaw raw[2];   // raw bytes of the current and the next k-step (index P, 1 − P)
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-
-    // prologue: super-block kt_begin / 4 whole in its buffer, X step kt_begin
-    // in stage 0, X step kt_begin + 1 and part 0 of the next super-block in
-    // register set 1
-    {
-        const int sb0 = kt_begin >> 2, k0 = kt_begin * BK;
-        u32x4 t[kRbPerThread];
-#pragma unroll
-        for (int i = 0; i < kRbPerThread; ++i) t[i] = buf_load16(rsb, goff[i] + (uint32_t)sb0 * 144u);
-        la.begin(0, k0, true);
-#pragma unroll
-        for (int i = 0; i < NA; ++i) la.load(0, i);
-        la.begin(1, k0 + BK, kt_begin + 1 < kt_end);
-#pragma unroll
-        for (int i = 0; i < NA; ++i) la.load(1, i);
-        const bool nlive = sb0 + 1 < sb_end;
-#pragma unroll
-        for (int i = RbPart<0>::lo; i < RbPart<0>::hi; ++i)
-            bv[1][i - RbPart<0>::lo] = buf_load16(rsb, nlive ? goff[i] + (uint32_t)(sb0 + 1) * 144u : kOOB);
-#pragma unroll
-        for (int i = 0; i < NA; ++i) la.store(0, i, A0);
-        u32x4 *B = (sb0 & 1) ? Bq1 : Bq0;
-#pragma unroll
-        for (int i = 0; i < kRbPerThread; ++i) B[threadIdx.x + kThreads * i] = t[i];
-        sync_lds();
-        rb_fetch<0>(B, lane, wave, raw[0]);
-    }
-
-    // Step kt (quarter C4, P = C4 & 1): X as in gemm_kernel; raw weights:
-    // slots 0..15 load part (C4 + 1) & 3 of the super-block that step kt + 1
-    // writes into set P, slots 16..31 write set 1 − P (part C4 of super-block
-    // kt / 4 + 1) to that super-block's buffer.
-    auto step = [&](auto C4c, int kt) MQ_INLINE {
-        constexpr int C4 = decltype(C4c)::value, P = C4 & 1;
-        constexpr int LC = (C4 + 1) & 3;
-        constexpr int NL = RbPart<LC>::hi - RbPart<LC>::lo, NS = RbPart<C4>::hi - RbPart<C4>::lo;
-        constexpr int H = 16;
-        u32x4 *An = P ? A0 : A1;
-        const int sb = kt >> 2;
-        const u32x4 *Bc = (sb & 1) ? Bq1 : Bq0;
-        u32x4 *Bn = (sb & 1) ? Bq0 : Bq1;
-        // the next step's raw bytes: this super-block's buffer, or for the
-        // last quarter the next one's, complete since the previous barrier
-        // (the last quarter writes no part)
-        static_assert(RbPart<3>::lo == RbPart<3>::hi, "the last quarter writes no part");
-        const u32x4 *Bnext = C4 == 3 ? Bn : Bc;
-        const int sbl = (kt + 1) / 4 + 1;
-        const uint32_t boff = sbl < sb_end ? (uint32_t)sbl * 144u : kOOB;
-        la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
-        rb_step<(C4 + 1) & 3>(P ? A1 : A0, Bnext, acc, lane, wave, raw[P], raw[1 - P],
-                              [&](auto SL) MQ_INLINE {
-            constexpr int sl = SL, half = sl < H ? sl : sl - H;
-            constexpr int TOT = sl < H ? NA + NL : NA + NS;
-            constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
-            static_for<hi - lo>([&](auto O) MQ_INLINE {
-                constexpr int o = lo + O;
-                if constexpr (sl < H) {
-                    if constexpr (o < NA) la.load(P, o);
-                    else bv[P][o - NA] = buf_load16(
-                        rsb, boff == kOOB ? kOOB : goff[RbPart<LC>::lo + o - NA] + boff);
-                } else {
-                    if constexpr (o < NA) la.store(1 - P, o, An);
-                    else Bn[threadIdx.x + kThreads * (RbPart<C4>::lo + o - NA)] = bv[1 - P][o - NA];
-                }
-            });
-        });
-        sync_lds();
-    };
-    for (int kt = kt_begin; kt < kt_end; kt += 4) {
-        step(std::integral_constant<int, 0>(), kt);
-        step(std::integral_constant<int, 1>(), kt + 1);
-        step(std::integral_constant<int, 2>(), kt + 2);
-        step(std::integral_constant<int, 3>(), kt + 3);
-    }
-
-    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
-}
-
-// ---------------------------------------------------------------------------
-// Fused Q6_K GEMM on 256 × 256 tiles, expanded in the MFMA operand registers
-// (the layout of gemm_q4k_rb_kernel: 1 × 4 waves, wave w owns weight rows
-// 64w .. 64w + 63 and all 256 activation rows).
-//
-// A Q6_K super-block of a 256-row tile is 53.8 KB, so two of them do not fit
-// in LDS beside the X stages; the unit staged here is a half super-block
-// (128 elements, two k-steps), 8 aligned 16-byte chunks per weight row:
-// chunks 0-3 the half's 64 low-nibble bytes, 4-5 its 32 high-pair bytes, 6
-// the block's 16 scales, 7 the block's last 16 bytes (d in bytes 14-15, so
-// no load reaches past the block's last dword).  The
-// blocks are only 2-byte aligned, so each chunk is loaded as the 20 aligned
-// bytes that contain it and shifted into place (realign16) before its LDS
-// write.  Thread t always stages chunk t mod 8 of rows t / 8 + 32i.  Rows
-// are 9 chunks apart in LDS: at 8 (128 bytes) the 32 rows one lane group
-// reads would share two bank groups; at 144 bytes they spread over 16.
-//
-// Lane l of wave w feeds weight rows 64w + 32f + (l & 31) at k = 16kk +
-// 8(l >> 5) + 0..7 of k-slice kk.  Within quarter c4 = 2h + C2 of the
-// super-block these are elements 128h + 64C2 + 16kk + 8(l >> 5) + 0..7, i.e.
-// group g = 2C2 + kk/2 and position p = 16(kk & 1) + 8(l >> 5) + 0..7: low
-// bits from half bytes 32(kk/2) + p (low nibbles for C2 = 0, high for
-// C2 = 1), high bits from half bytes p of the qh part shifted by 2g, scale
-// 8h + 4C2 + kk.  Value (d·s)·(q − 32) in f32, as the decode (q6k_chunk).
-//
-// Pipeline: X as in gemm_kernel.  Raw weights: two half-super-block buffers;
-// during the two k-steps of half hx the 8 chunks per thread of half hx + 1
-// are loaded (4 per step, one step ahead in a register set) and written to
-// the other buffer, last read in half hx − 1.  K ranges start on even steps.
-// ---------------------------------------------------------------------------
-constexpr int kR6Chunks = 256 * 8;                  // 16-byte chunks of a tile half super-block
-constexpr int kR6Stride = 9;                        // LDS chunks per row
-constexpr int kR6PerThread = kR6Chunks / kThreads;  // 8
-static_assert(kR6PerThread * kThreads == kR6Chunks, "chunks per thread");
-
-// The lane's bytes of one k-step for its two weight rows, and the four
-// factors d·s of its k-slices.
-struct R6Raw {
-    u32x2 ql[2][4], qh[2][2];
-    float ds[2][4];
-};
-
-// h: the half of the super-block the step lies in; C2: its quarter in the half.
-template <int C2>
-__device__ __forceinline__ void r6_fetch(const u32x4 *Bc, int h, int lane, int wave, R6Raw &r) {
-    const int hl = lane >> 5;
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * kR6Stride;
-        const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) r.ql[f][kk] = q2[4 * (kk >> 1) + 2 * (kk & 1) + hl];
-        const u32x2 *h2 = reinterpret_cast<const u32x2 *>(blk + 4);
-        r.qh[f][0] = h2[hl];
-        r.qh[f][1] = h2[2 + hl];
-        const uint32_t sw = reinterpret_cast<const uint32_t *>(blk + 6)[2 * h + C2];
-        const float d = f16_bits_to_f32(reinterpret_cast<const uint32_t *>(blk + 7)[3] >> 16);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) r.ds[f][kk] = d * (float)(int)(int8_t)(sw >> (8 * kk));
-    }
-}
-
-template <int C2, int KK>
-__device__ __forceinline__ half8 q6k_frag(const R6Raw &r, int f) {
-    constexpr uint32_t L = 0x0F0F0F0Fu, H = 0x03030303u;
-    constexpr uint32_t n4 = 4 * C2, h2 = 4 * C2 + 2 * (KK >> 1);
-    const u32x2 l = r.ql[f][KK], hb = r.qh[f][KK & 1];
-    const uint32_t q0 = ((l.x >> n4) & L) | (((hb.x >> h2) & H) << 4);
-    const uint32_t q1 = ((l.y >> n4) & L) | (((hb.y >> h2) & H) << 4);
-    return __builtin_bit_cast(half8, q6k_chunk(q0, q1, r.ds[f][KK]));
-}
-
-template <int C2, class Slot>
-__device__ __forceinline__ void rb6_step(const u32x4 *Ac, const u32x4 *Bc, int h,
-                                         f32x16 (&acc)[8][2], int lane, int wave, Slot &&slot) {
-    const int hl = lane >> 5;
-    R6Raw raw;
-    r6_fetch<C2>(Bc, h, lane, wave, raw);
-    half8 af[2][8], bf[2][2];
-    auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
-        constexpr int kk = KKc;
-        const int c = kk * 2 + hl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = i * 32 + (lane & 31);
-            dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
-        }
-    };
-    load_a(std::integral_constant<int, 0>(), af[0]);
-    bf[0][0] = q6k_frag<C2, 0>(raw, 0);
-    bf[0][1] = q6k_frag<C2, 0>(raw, 1);
-    static_for<4>([&](auto KK) MQ_INLINE {
-        constexpr int kk = KK, c = kk & 1;
-        if constexpr (kk + 1 < 4) {
-            load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
-            bf[c ^ 1][0] = q6k_frag<C2, kk + 1>(raw, 0);
-            bf[c ^ 1][1] = q6k_frag<C2, kk + 1>(raw, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<16>([&](auto IJ) MQ_INLINE {
-            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 16 + IJ;
-            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
-                                                               0);
-            if constexpr (n & 1) {
-                __builtin_amdgcn_sched_barrier(0);
-                slot(std::integral_constant<int, n / 2>());
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        });
-    });
-}
-
-template <int FMT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
-    static_assert(FMT == kFmtQ6_K, "Q6_K only");
-    constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
-    constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
-    __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
-    __shared__ u32x4 Bq0[256 * kR6Stride], Bq1[256 * kR6Stride];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = 0, wn = wave;
-    const int pid = blockIdx.x;
-    int tile, part = 0;
-    if (pid < a.dp_tiles) {
-        tile = xcd_remap(pid, a.dp_tiles);
-    } else {
-        const int j = xcd_remap(pid - a.dp_tiles, (int)gridDim.x - a.dp_tiles);
-        const int tt = j % a.tail_tiles;
-        tile = a.dp_tiles + tt;
-        part = j / a.tail_tiles;
-    }
-    const bool tail = pid >= a.dp_tiles;
-    int tm, tn;
-    tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    // K ranges start on even steps and (K a multiple of 256) end on even ones
-    const int kt_begin = tail ? part * a.steps_per_split : 0;
-    const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
-    const int hx_end = kt_end >> 1;
-
-    F16Loader<BM> la;
-    la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
-    constexpr int NA = decltype(la)::NPART;
-    // raw weight chunks: the resource starts at the 16-byte boundary at or
-    // below the tile's first row; chunk p = thread mod 8 of rows r0 + 32i
-    const int rows_valid = min(BN, a.N - n0);
-    const int64_t start = (int64_t)n0 * a.ldw;
-    const uint32_t shift0 = (uint32_t)(((uintptr_t)a.W + start) & 15);
-    const int64_t extent = shift0 + (int64_t)rows_valid * a.ldw;
-    const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(a.W + start - shift0, (uint32_t)((extent + 3) & ~(int64_t)3));
-    const int p = (int)threadIdx.x & 7, r0 = (int)threadIdx.x >> 3;
-    const uint32_t psrc0 = p < 4 ? 16u * p : (p < 6 ? 128u + 16u * (p - 4) : (p == 6 ? 192u : 194u));
-    const uint32_t phalf = p < 4 ? 64u : (p < 6 ? 32u : 0u);   // + phalf·h for half h
-    uint32_t roff[kR6PerThread];
-#pragma unroll
-    for (int i = 0; i < kR6PerThread; ++i) roff[i] = shift0 + (uint32_t)((r0 + 32 * i) * a.ldw) + psrc0;
-    uint32_t bv[2][4][5], bsh[2][4];
-    // load chunk i of half hx into slot (set, j)
-    auto bload = [&](int set, int j, int i, int hx) MQ_INLINE {
-        const uint32_t o = hx < hx_end ? roff[i] + (uint32_t)(hx >> 1) * 210u + phalf * (hx & 1)
-                                       : kOOB;
-        bsh[set][j] = o & 2;
-        load5(rsb, o, bv[set][j]);
-    };
-    auto bstore = [&](int set, int j, int i, u32x4 *buf) MQ_INLINE {
-        buf[(r0 + 32 * i) * kR6Stride + p] = realign16(bv[set][j], bsh[set][j]);
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-
-    // prologue: half kt_begin / 2 whole in its buffer, X step kt_begin in
-    // stage 0, X step kt_begin + 1 and part 0 of the next half in set 1
-    {
-        const int hx0 = kt_begin >> 1, k0 = kt_begin * BK;
-        u32x4 *B = (hx0 & 1) ? Bq1 : Bq0;
-        la.begin(0, k0, true);
-#pragma unroll
-        for (int i = 0; i < NA; ++i) la.load(0, i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bload(0, i, i, hx0);
-        la.begin(1, k0 + BK, kt_begin + 1 < kt_end);
-#pragma unroll
-        for (int i = 0; i < NA; ++i) la.load(1, i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bstore(0, i, i, B);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bload(0, i, 4 + i, hx0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bload(1, i, i, hx0 + 1);
-#pragma unroll
-        for (int i = 0; i < NA; ++i) la.store(0, i, A0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bstore(0, i, 4 + i, B);
-        sync_lds();
-    }
-
-    // Step kt (C2 = kt & 1 = P): slots 0..15 load part 1 − C2 of the half
-    // that step kt + 1 writes (half kt/2 + 1 for C2 = 0, kt/2 + 2 for C2 = 1)
-    // into set P; slots 16..31 write set 1 − P (part C2 of half kt/2 + 1).
-    auto step = [&](auto C2c, int kt) MQ_INLINE {
-        constexpr int C2 = decltype(C2c)::value, P = C2;
-        constexpr int H = 16, NB = 4;
-        u32x4 *An = P ? A0 : A1;
-        const int hx = kt >> 1;
-        const u32x4 *Bc = (hx & 1) ? Bq1 : Bq0;
-        u32x4 *Bn = (hx & 1) ? Bq0 : Bq1;
-        const int hl_next = C2 == 0 ? hx + 1 : hx + 2;
-        constexpr int lpart = 1 - C2;
-        la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
-        rb6_step<C2>(P ? A1 : A0, Bc, hx & 1, acc, lane, wave, [&](auto SL) MQ_INLINE {
-            constexpr int sl = SL, half = sl < H ? sl : sl - H;
-            constexpr int TOT = NA + NB;
-            constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
-            static_for<hi - lo>([&](auto O) MQ_INLINE {
-                constexpr int o = lo + O;
-                if constexpr (sl < H) {
-                    if constexpr (o < NA) la.load(P, o);
-                    else bload(P, o - NA, 4 * lpart + (o - NA), hl_next);
-                } else {
-                    if constexpr (o < NA) la.store(1 - P, o, An);
-                    else bstore(1 - P, o - NA, 4 * C2 + (o - NA), Bn);
-                }
-            });
-        });
-        sync_lds();
-    };
-    for (int kt = kt_begin; kt < kt_end; kt += 2) {
-        step(std::integral_constant<int, 0>(), kt);
-        step(std::integral_constant<int, 1>(), kt + 1);
-    }
-    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
-}
+namespace mq {
+namespace {
 
 // Y tile = Σ_s partial[s] in the order s = 0, 1, ..., split − 1, for every
 // tail tile.  Block (tail tile, chunk) handles 1024 consecutive elements of
