@@ -154,6 +154,28 @@ def test_random_tolerance_and_cache_identity(fmt, M, N, K):
     assert np.array_equal(Yf1, Yc1), f"fused and cache paths differ: max {np.abs(Yf1 - Yc1).max()}"
 
 
+@pytest.mark.parametrize("fmt", [0, 12, 14])
+def test_large_m_exact(fmt):
+    """M = 16400 tokens (65 M-tiles, the last 16 rows deep): 1040 tiles of
+    256 × 256 over N = 4096, four whole rounds and a K-split tail of 16 tiles;
+    cache GEMM (fmt 0, on the decoded weight) and both register-expansion
+    fused kernels.  Integer inputs: sampled rows exact, including the last."""
+    M, N, K = 16400, 4096, 512
+    wf = 12 if fmt == 0 else fmt
+    q = synth.weights(wf, synth.rng(39, 0, wf, 0), N, K, mode="integer")
+    x = synth.activations(synth.rng(39, role=1), M, K, mode="integer")
+    w16 = oracle.dequant_ref(wf, q, N, K)
+    if fmt == 0:
+        announce("gemm_f16cache", f"M={M} N={N} K={K}")
+        Y = to_host(mq.gemm_f16cache(to_dev_f16(x), to_dev_f16(w16), K))
+    else:
+        Y = to_host(_fused(fmt, x, q, N, K))
+    rows = np.unique(np.concatenate([[0, 255, 16383, 16384, M - 1],
+                                     np.random.default_rng(39).choice(M, 11)]))
+    Yref, _ = oracle.gemm_ref(x[rows], w16)
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
+
+
 SHAPES_7B = [("q/o", 12, 3584, 3584), ("k/v", 12, 512, 3584), ("gate/up", 12, 18944, 3584),
              ("down", 14, 3584, 18944)]
 
