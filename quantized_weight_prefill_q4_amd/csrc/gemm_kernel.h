@@ -819,8 +819,7 @@ __device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN],
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int FMT, bool XF32, int NWV = 4>
 __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
-    static_assert(NWV == 4 || (NWV == 8 && BN == 128 && FMT == kFmtF16 && !XF32),
-                  "8 waves: f16-cache tiles of 128 columns");
+    static_assert(NWV == 4 || (NWV == 8 && BN == 128 && !XF32), "8 waves: tiles of 128 columns");
     constexpr int BK = 64;
     constexpr int WN = NWV == 4 ? 2 : (BM >= 128 ? 2 : 4), WM = NWV / WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -856,7 +855,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         la.init((const float *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
     else
         la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
-    std::conditional_t<NWV == 4, typename BLoaderFor<BN, FMT>::T, F16Loader<BN, 64 * NWV>> lb;
+    // The fused B loaders are written for 256 threads: with 8 waves, waves
+    // 0-3 run them (the condition is uniform per wave) and all 8 stage X.
+    std::conditional_t<NWV == 4 || FMT != kFmtF16, typename BLoaderFor<BN, FMT>::T,
+                       F16Loader<BN, 64 * NWV>>
+        lb;
+    const bool bw = NWV == 4 || FMT == kFmtF16 ||
+                    __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) < kThreads / 64;
     if constexpr (FMT == kFmtF16)
         lb.init((const uint16_t *)a.W + n0 * a.ldw, min(BN, a.N - n0), a.ldw, a.K);
     else
@@ -878,17 +883,20 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.load(0, i);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) lb.load(0, i);
+        for (int i = 0; i < NB; ++i)
+            if (bw) lb.load(0, i);
         la.begin(1, k0 + BK, has1);
         lb.begin(1, k0 + BK, has1);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.load(1, i);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) lb.load(1, i);
+        for (int i = 0; i < NB; ++i)
+            if (bw) lb.load(1, i);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.store(0, i, A0);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) lb.store(0, i, B0);
+        for (int i = 0; i < NB; ++i)
+            if (bw) lb.store(0, i, B0);
         sync_lds();
     }
 
@@ -910,10 +918,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
                 constexpr int o = lo + O;
                 if constexpr (sl < H) {
                     if constexpr (o < NA) la.load(P, o);
-                    else lb.load(P, o - NA);
+                    else if (bw) lb.load(P, o - NA);
                 } else {
                     if constexpr (o < NA) la.store(1 - P, o, An);
-                    else lb.store(1 - P, o - NA, Bn);
+                    else if (bw) lb.store(1 - P, o - NA, Bn);
                 }
             });
         });
@@ -969,9 +977,13 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ w
 
 template <int BM, int BN, int FMT, bool XF32>
 hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
-    // f16-cache tiles of 128 columns on 8 waves (measured 1.5-4% faster at
-    // M = 128 and on the 7B q/o shape; no slower elsewhere)
-    constexpr int NWV = (BN == 128 && FMT == kFmtF16 && !XF32) ? 8 : 4;
+    // Tiles of 128 columns on 8 waves: two waves per SIMD double the LDS
+    // throughput a step can draw on.  f16 cache: 1.5-4% faster at M = 128
+    // and on the 7B q/o shape, no slower elsewhere.  Fused, with 128 or 256
+    // rows: 3-7% faster at M = 2048 (q/o, 4096 x 4096; Q4_K, Q6_K, Q8_0),
+    // 17% at M = 128; not on 64-row tiles, whose 32 x 32 wave tiles leave too
+    // little MFMA work beside the decode (k/v at M = 2048: 20% slower).
+    constexpr int NWV = (BN == 128 && !XF32 && (FMT == kFmtF16 || BM >= 128)) ? 8 : 4;
     hipLaunchKernelGGL((gemm_kernel<BM, BN, FMT, XF32, NWV>), dim3(grid), dim3(64 * NWV), 0, stream,
                        a);
     return hipGetLastError();
