@@ -857,6 +857,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
     // The fused B loaders are written for 256 threads: with 8 waves, waves
     // 0-3 run them (the condition is uniform per wave) and all 8 stage X.
+    // Waves 4-7 still issue the B loads, at out-of-range offsets that read
+    // zeros, and skip only the LDS writes: with the loads under a branch the
+    // compiler's wait counts had to cover both paths and made the decoding
+    // waves wait for the loads of the current step (M = 128: 14336 x 4096
+    // Q8_0 41 -> 52 us).
     std::conditional_t<NWV == 4 || FMT != kFmtF16, typename BLoaderFor<BN, FMT>::T,
                        F16Loader<BN, 64 * NWV>>
         lb;
@@ -879,19 +884,17 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         const int k0 = kt_begin * BK;
         const bool has1 = kt_begin + 1 < kt_end;
         la.begin(0, k0, true);
-        lb.begin(0, k0, true);
+        lb.begin(0, k0, bw);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.load(0, i);
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-            if (bw) lb.load(0, i);
+        for (int i = 0; i < NB; ++i) lb.load(0, i);
         la.begin(1, k0 + BK, has1);
-        lb.begin(1, k0 + BK, has1);
+        lb.begin(1, k0 + BK, has1 && bw);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.load(1, i);
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-            if (bw) lb.load(1, i);
+        for (int i = 0; i < NB; ++i) lb.load(1, i);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.store(0, i, A0);
 #pragma unroll
@@ -910,7 +913,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         u32x4 *An = P ? A0 : A1, *Bn = P ? B0 : B1;
         const bool live2 = kt + 2 < kt_end;
         la.begin(P, (kt + 2) * BK, live2);
-        lb.begin(P, (kt + 2) * BK, live2);
+        lb.begin(P, (kt + 2) * BK, live2 && bw);
         mma_step<FM, FN, TM, TN>(P ? A1 : A0, P ? B1 : B0, acc, wm, wn, lane, [&](auto SL) MQ_INLINE {
             constexpr int sl = SL, half = sl < H ? sl : sl - H;
             constexpr int lo = half * (NA + NB) / H, hi = (half + 1) * (NA + NB) / H;
@@ -918,7 +921,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
                 constexpr int o = lo + O;
                 if constexpr (sl < H) {
                     if constexpr (o < NA) la.load(P, o);
-                    else if (bw) lb.load(P, o - NA);
+                    else lb.load(P, o - NA);
                 } else {
                     if constexpr (o < NA) la.store(1 - P, o, An);
                     else if (bw) lb.store(1 - P, o - NA, Bn);
@@ -980,9 +983,9 @@ hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
     // Tiles of 128 columns on 8 waves: two waves per SIMD double the LDS
     // throughput a step can draw on.  f16 cache: 1.5-4% faster at M = 128
     // and on the 7B q/o shape, no slower elsewhere.  Fused, with 128 or 256
-    // rows: 3-7% faster at M = 2048 (q/o, 4096 x 4096; Q4_K, Q6_K, Q8_0),
-    // 17% at M = 128; not on 64-row tiles, whose 32 x 32 wave tiles leave too
-    // little MFMA work beside the decode (k/v at M = 2048: 20% slower).
+    // rows: 2-5% faster at M = 2048 (q/o, 4096 x 4096; Q4_K, Q6_K, Q8_0),
+    // 2-18% at M = 128, no slower elsewhere.  Fused 64-row tiles keep 4
+    // waves (8 gained nothing on k/v and lost 3% at N = 1024).
     constexpr int NWV = (BN == 128 && !XF32 && (FMT == kFmtF16 || BM >= 128)) ? 8 : 4;
     hipLaunchKernelGGL((gemm_kernel<BM, BN, FMT, XF32, NWV>), dim3(grid), dim3(64 * NWV), 0, stream,
                        a);
