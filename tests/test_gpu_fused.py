@@ -22,7 +22,7 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 
 import quantized_weight_prefill_q4_amd as mq  # noqa: E402
 
-FMT_NAME = {12: "Q4_K", 14: "Q6_K", 8: "Q8_0"}
+FMT_NAME = {12: "Q4_K", 14: "Q6_K", 8: "Q8_0", 2: "Q4_0", 6: "Q5_0", 7: "Q5_1", 13: "Q5_K"}
 
 
 def _fused(fmt, x_bits, q, N, K, split_k=0):
@@ -50,6 +50,23 @@ def test_integer_exact(fmt, M, N, K, split):
     Y = to_host(_fused(fmt, x, q, N, K, split_k=split))
     Yref, _ = oracle.gemm_ref(x, oracle.dequant_ref(fmt, q, N, K))
     assert np.array_equal(Y.astype(np.float64), Yref)
+
+
+@pytest.mark.parametrize("fmt", [2, 6, 7, 8, 12, 13, 14])
+@pytest.mark.parametrize("M,N,K,split", [(700, 2900, 1536, 0), (700, 2900, 1536, 1),
+                                         (97, 390, 1024, 0), (97, 390, 1024, 3)])
+def test_eight_wave_tiles_integer_exact(fmt, M, N, K, split):
+    """Tiles of 128 columns with 256 rows (M = 700: 69 tiles, split 3 ways
+    along K by the plan, or whole) and with 128 rows (M = 97) run on 8 waves,
+    waves 0-3 decoding the weights: every format, ragged in M and N, exact
+    with integer inputs on sampled rows."""
+    q = synth.weights(fmt, synth.rng(38, 0, fmt, M), N, K, mode="integer")
+    x = synth.activations(synth.rng(38, role=1), M, K, mode="integer")
+    Y = to_host(_fused(fmt, x, q, N, K, split_k=split))
+    edges = np.array([0, 63, 64, 127, 128, 255, 256, 511, 512, M - 1])
+    rows = np.unique(np.concatenate([edges[edges < M], np.random.default_rng(M).choice(M, 12)]))
+    Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(fmt, q, N, K))
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
 
 
 @pytest.mark.parametrize("fmt", [12, 8])
