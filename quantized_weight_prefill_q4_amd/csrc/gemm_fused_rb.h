@@ -545,5 +545,254 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
     store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused Q8_0 GEMM on 256 × 256 tiles, expanded in the MFMA operand registers
+// (the layout of gemm_q6k_rb_kernel).  For K a multiple of 256 only: a row is
+// then K/256 runs of 8 blocks of 272 bytes, so every row starts on a 16-byte
+// boundary.
+//
+// The 2×2 loader reads each lane's 34-byte block as three loads (16 + 16 + 4
+// aligned bytes), and every one of them touches the 1-2 lines of 32 rows: the
+// L1 sees each line three times.  Here the unit staged in LDS is half a run
+// (4 blocks, 136 bytes, two k-steps): the 9 aligned 16-byte chunks that cover
+// it (a half starts 8 bytes into a chunk when it is odd), loaded once each,
+// consecutive threads on consecutive chunks of a row.  Thread t stages chunks
+// c = t + 256i (i < 9) of the tile's 256 × 9, row c / 9, chunk c mod 9, at
+// LDS position c: rows are 144 bytes apart, which spreads the 32 rows a lane
+// group reads over 16 bank groups.
+//
+// Lane l of wave w feeds weight rows 64w + 32f + (l & 31) at k = 16kk +
+// 8(l >> 5) + 0..7 of k-slice kk.  Within step C2 of the half these are
+// block b = 2C2 + kk/2, bytes 2 + 16(kk & 1) + 8(l >> 5) + 0..7, with the
+// block's d in its bytes 0-1.  Block b starts at byte 34b + o of the staged
+// row (o = 8 for odd halves), so the 8 bytes are 2 bytes past a dword for
+// even b (three dwords, realigned) and dword-aligned for odd b.  Value d·q in
+// f32, rounded once to f16, as the decode (q80_chunk).
+//
+// Pipeline as gemm_q6k_rb_kernel: two half buffers; during the two k-steps
+// of half hx the 9 chunks per thread of half hx + 1 are loaded (5, then 4,
+// one step ahead in a register set) and written to the other buffer, last
+// read in half hx − 1.  K ranges start on even steps.
+// ---------------------------------------------------------------------------
+constexpr int kR8Stride = 9;                             // LDS chunks per row
+constexpr int kR8PerThread = 256 * kR8Stride / kThreads;  // 9
+static_assert(kR8PerThread * kThreads == 256 * kR8Stride, "chunks per thread");
+
+// Chunks [lo, hi) of the thread's 9 belong to part c (5 + 4).
+template <int C>
+struct R8Part {
+    static constexpr int lo = C == 0 ? 0 : 5, hi = C == 0 ? 5 : kR8PerThread;
+};
+
+// The lane's quant dwords of one k-step for its two weight rows (per
+// k-slice) and the two blocks' d.
+struct R8Raw {
+    uint32_t q[2][4][2];
+    float d[2][2];
+};
+
+// o4: the staged row's first block at dword o4 (0, or 2 for odd halves).
+template <int C2>
+__device__ __forceinline__ void r8_fetch(const u32x4 *Bc, int o4, int lane, int wave, R8Raw &r) {
+    const int hl = lane >> 5;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const uint32_t *rw =
+            reinterpret_cast<const uint32_t *>(Bc + (wave * 64 + f * 32 + (lane & 31)) * kR8Stride) +
+            o4;
+        // block 2C2 (even): d at byte 68C2, quants from byte 68C2 + 2
+        constexpr int be = 17 * C2;   // its first dword
+        // block 2C2 + 1 (odd): d at byte 68C2 + 34 (dword be + 8, upper half),
+        // quants from byte 68C2 + 36 (dword be + 9)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const uint32_t *w = rw + be + 4 * kk + 2 * hl;
+            const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+            r.q[f][kk][0] = __builtin_amdgcn_alignbyte(w1, w0, 2);
+            r.q[f][kk][1] = __builtin_amdgcn_alignbyte(w2, w1, 2);
+        }
+#pragma unroll
+        for (int kk = 2; kk < 4; ++kk) {
+            const uint32_t *w = rw + be + 9 + 4 * (kk - 2) + 2 * hl;
+            r.q[f][kk][0] = w[0];
+            r.q[f][kk][1] = w[1];
+        }
+        r.d[f][0] = f16_bits_to_f32(rw[be]);
+        r.d[f][1] = f16_bits_to_f32(rw[be + 8] >> 16);
+    }
+}
+
+template <int KK>
+__device__ __forceinline__ half8 q80_frag(const R8Raw &r, int f) {
+    return __builtin_bit_cast(half8, q80_chunk(r.q[f][KK][0], r.q[f][KK][1], r.d[f][KK >> 1]));
+}
+
+template <int C2, class Slot>
+__device__ __forceinline__ void rb8_step(const u32x4 *Ac, const u32x4 *Bc, int o4,
+                                         f32x16 (&acc)[8][2], int lane, int wave, Slot &&slot) {
+    const int hl = lane >> 5;
+    R8Raw raw;
+    r8_fetch<C2>(Bc, o4, lane, wave, raw);
+    half8 af[2][8], bf[2][2];
+    auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
+        constexpr int kk = KKc;
+        const int c = kk * 2 + hl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = i * 32 + (lane & 31);
+            dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
+        }
+    };
+    load_a(std::integral_constant<int, 0>(), af[0]);
+    bf[0][0] = q80_frag<0>(raw, 0);
+    bf[0][1] = q80_frag<0>(raw, 1);
+    static_for<4>([&](auto KK) MQ_INLINE {
+        constexpr int kk = KK, c = kk & 1;
+        if constexpr (kk + 1 < 4) {
+            load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
+            bf[c ^ 1][0] = q80_frag<kk + 1>(raw, 0);
+            bf[c ^ 1][1] = q80_frag<kk + 1>(raw, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<16>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 16 + IJ;
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
+                                                               0);
+            if constexpr (n & 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                slot(std::integral_constant<int, n / 2>());
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    });
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_q80_rb_kernel(Args a) {
+    static_assert(FMT == kFmtQ8_0, "Q8_0 only");
+    constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
+    constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
+    __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
+    __shared__ u32x4 Bq0[256 * kR8Stride], Bq1[256 * kR8Stride];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = 0, wn = wave;
+    const int pid = blockIdx.x;
+    int tile, part = 0;
+    if (pid < a.dp_tiles) {
+        tile = xcd_remap(pid, a.dp_tiles);
+    } else {
+        const int j = xcd_remap(pid - a.dp_tiles, (int)gridDim.x - a.dp_tiles);
+        const int tt = j % a.tail_tiles;
+        tile = a.dp_tiles + tt;
+        part = j / a.tail_tiles;
+    }
+    const bool tail = pid >= a.dp_tiles;
+    int tm, tn;
+    tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    // K ranges start on even steps and (K a multiple of 256) end on even ones
+    const int kt_begin = tail ? part * a.steps_per_split : 0;
+    const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
+    const int hx_end = kt_end >> 1;
+
+    F16Loader<BM> la;
+    la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
+    constexpr int NA = decltype(la)::NPART;
+    // raw weight chunks (rows 16-byte aligned): chunk c = t + 256i of the
+    // tile's 256 × 9 is row c / 9, chunk c mod 9, LDS position c
+    const int rows_valid = min(BN, a.N - n0);
+    const __amdgpu_buffer_rsrc_t rsb =
+        make_rsrc(a.W + (int64_t)n0 * a.ldw, (uint32_t)(rows_valid * a.ldw));
+    const int t = (int)threadIdx.x;
+    uint32_t roff[kR8PerThread];
+#pragma unroll
+    for (int i = 0; i < kR8PerThread; ++i) {
+        const int c = t + kThreads * i, row = c / kR8Stride;
+        roff[i] = (uint32_t)(row * a.ldw) + 16u * (uint32_t)(c - row * kR8Stride);
+    }
+    u32x4 bv[2][5];
+    // load chunk i of half hx into slot (set, j): the half's bytes start at
+    // 136·hx, in the chunk at or below it
+    auto bload = [&](int set, int j, int i, int hx) MQ_INLINE {
+        const uint32_t o = hx < hx_end ? roff[i] + ((136u * (uint32_t)hx) & ~15u) : kOOB;
+        bv[set][j] = buf_load16(rsb, o);
+    };
+    auto bstore = [&](int set, int j, int i, u32x4 *buf) MQ_INLINE {
+        buf[t + kThreads * i] = bv[set][j];
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    // prologue: half kt_begin / 2 whole in its buffer, X step kt_begin in
+    // stage 0, X step kt_begin + 1 and part 0 of the next half in set 1
+    {
+        const int hx0 = kt_begin >> 1, k0 = kt_begin * BK;
+        u32x4 *B = (hx0 & 1) ? Bq1 : Bq0;
+        la.begin(0, k0, true);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.load(0, i);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) bload(0, i, i, hx0);
+        la.begin(1, k0 + BK, kt_begin + 1 < kt_end);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.load(1, i);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) bstore(0, i, i, B);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bload(0, i, 5 + i, hx0);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) bload(1, i, i, hx0 + 1);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) la.store(0, i, A0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bstore(0, i, 5 + i, B);
+        sync_lds();
+    }
+
+    // Step kt (C2 = kt & 1 = P): slots 0..15 load part 1 − C2 of the half
+    // that step kt + 1 writes (half kt/2 + 1 for C2 = 0, kt/2 + 2 for C2 = 1)
+    // into set P; slots 16..31 write set 1 − P (part C2 of half kt/2 + 1).
+    auto step = [&](auto C2c, int kt) MQ_INLINE {
+        constexpr int C2 = decltype(C2c)::value, P = C2;
+        constexpr int H = 16;
+        constexpr int lpart = 1 - C2;
+        constexpr int NBL = R8Part<lpart>::hi - R8Part<lpart>::lo;
+        constexpr int NBS = R8Part<C2>::hi - R8Part<C2>::lo;
+        u32x4 *An = P ? A0 : A1;
+        const int hx = kt >> 1;
+        const u32x4 *Bc = (hx & 1) ? Bq1 : Bq0;
+        u32x4 *Bn = (hx & 1) ? Bq0 : Bq1;
+        const int hl_next = C2 == 0 ? hx + 1 : hx + 2;
+        la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
+        rb8_step<C2>(P ? A1 : A0, Bc, 2 * (hx & 1), acc, lane, wave, [&](auto SL) MQ_INLINE {
+            constexpr int sl = SL, half = sl < H ? sl : sl - H;
+            constexpr int TOT = NA + (sl < H ? NBL : NBS);
+            constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
+            static_for<hi - lo>([&](auto O) MQ_INLINE {
+                constexpr int o = lo + O;
+                if constexpr (sl < H) {
+                    if constexpr (o < NA) la.load(P, o);
+                    else bload(P, o - NA, R8Part<lpart>::lo + (o - NA), hl_next);
+                } else {
+                    if constexpr (o < NA) la.store(1 - P, o, An);
+                    else bstore(1 - P, o - NA, R8Part<C2>::lo + (o - NA), Bn);
+                }
+            });
+        });
+        sync_lds();
+    };
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
+        step(std::integral_constant<int, 0>(), kt);
+        step(std::integral_constant<int, 1>(), kt + 1);
+    }
+    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+}
+
 }  // namespace
 }  // namespace mq

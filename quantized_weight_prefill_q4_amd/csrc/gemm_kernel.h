@@ -34,8 +34,9 @@
 // store the f16 tile to LDS: each weight element is expanded once per block
 // tile (⌈M/BM⌉ times in all), not once per wave.  Fused Q4_K and Q6_K on
 // 256 × 256 tiles have kernels of their own (gemm_q4k_rb_kernel,
-// gemm_q6k_rb_kernel, below) that stage raw (half) super-blocks in LDS and
-// expand them in the MFMA operand registers.
+// gemm_q6k_rb_kernel, gemm_q80_rb_kernel for K a multiple of 256, below) that
+// stage raw (half) super-blocks or block runs in LDS and expand them in the
+// MFMA operand registers.
 
 #pragma once
 
@@ -1004,6 +1005,13 @@ hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t strea
         } else if constexpr (FMT == kFmtQ6_K && !XF32) {
             hipLaunchKernelGGL(gemm_q6k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
             return hipGetLastError();
+        } else if constexpr (FMT == kFmtQ8_0 && !XF32) {
+            if (a.K % 256 == 0) {   // rows of whole 272-byte runs: 16-byte aligned
+                hipLaunchKernelGGL(gemm_q80_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream,
+                                   a);
+                return hipGetLastError();
+            }
+            return launch_tile<256, 256, FMT, XF32>(a, grid, stream);
         } else if constexpr (!XF32) {
             return launch_tile<256, 256, FMT, XF32>(a, grid, stream);
         }

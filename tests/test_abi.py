@@ -221,9 +221,12 @@ def test_workspace_planning(L):
         assert L.mq_gemm_workspace_bytes(fmt, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
     # the Q4_K 256 x 256 kernel stages whole super-blocks: its K ranges are
     # multiples of 4 k-steps, so a requested 7-way split of 20 steps becomes
-    # 5 ranges of 4 (Q8_0, same tiles, keeps 7 ranges of 3, the last of 2)
+    # 5 ranges of 4.  The Q8_0 one (K a multiple of 256) pairs k-steps: 7
+    # ranges of 3 become 5 of 4 (ranges start even); with K = 1056 (17 steps)
+    # Q8_0 keeps the 2 x 2 kernel and 6 ranges of 3, the last of 2
     assert L.mq_gemm_workspace_bytes(12, 300, 32768, 1280, 7) == 5 * 256 * 256 * 256 * 4
-    assert L.mq_gemm_workspace_bytes(8, 300, 32768, 1280, 7) == 7 * 256 * 256 * 256 * 4
+    assert L.mq_gemm_workspace_bytes(8, 300, 32768, 1280, 7) == 5 * 256 * 256 * 256 * 4
+    assert L.mq_gemm_workspace_bytes(8, 300, 32768, 1056, 7) == 6 * 256 * 256 * 256 * 4
     assert L.mq_gemm_workspace_bytes(12, 300, 32768, 1280, 3) == 3 * 256 * 256 * 256 * 4
     # 4096 x 14336 at M = 1024: 64 tiles of 256 x 256 split 4 ways (ranges of
     # 3584 k fill the compute units); at M = 512 the ranges would be 1792 k, so
