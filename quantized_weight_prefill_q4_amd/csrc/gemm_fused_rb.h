@@ -1,6 +1,6 @@
-// Fused GEMM kernels that expand Q4_K / Q6_K weights straight into the MFMA
-// operand registers (256 × 256 tiles).  Included by gemm_kernel.h, whose
-// helpers (loaders, swizzle, tile mapping, store_tile) they use.
+// Fused GEMM kernels that expand Q4_K / Q6_K / Q8_0 weights straight into
+// the MFMA operand registers (256 × 256 tiles).  Included by gemm_kernel.h,
+// whose helpers (loaders, swizzle, tile mapping, store_tile) they use.
 //
 // minfer "05 · 8p — Persistent f16 weight cache + fused dequant-in-GEMM" §2
 // and §3.3: the fused shape reads the quantized bytes of each B tile and
