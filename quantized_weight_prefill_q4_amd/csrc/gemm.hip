@@ -41,10 +41,17 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
     // times the tiles, so a two-way K split instead of eight fills the
     // compute units, with a quarter of the partial-plane traffic (k/v at
     // M = 2048: 30.5 -> 26.2 us).  Not for long K: a 64-row tile's k-loop is
-    // latency-bound (M = 512, N = 4096, K = 14336: 78 -> 124 us).
+    // latency-bound (M = 512, N = 4096, K = 14336: 78 -> 124 us).  The fused
+    // kernels decode the weights once per row tile, so they take 128-row
+    // tiles instead while those still number kCUs / 4 (a K split of at most
+    // 4): k/v at M = 2048 Q4_K 28.7 -> 26.3 us, Q6_K 36.4 -> 30.5, Q8_0
+    // 28.7 -> 27.2; N = 1024 46.3 -> 42.0; M = 512, N = 2048 31.2 -> 28.7.
     if (p.bn == 128 && M > 128 && K <= 4096 &&
-        (int64_t)((M + 255) / 256) * ((N + 127) / 128) * 4 <= kCUs)
-        p.bm = 64;
+        (int64_t)((M + 255) / 256) * ((N + 127) / 128) * 4 <= kCUs) {
+        const bool rows128 =
+            fmt != kFmtF16 && (int64_t)((M + 127) / 128) * ((N + 127) / 128) * 4 >= kCUs;
+        p.bm = rows128 ? 128 : 64;
+    }
     p.tiles_m = (M + p.bm - 1) / p.bm;
     p.tiles_n = (N + p.bn - 1) / p.bn;
     const int tiles = p.tiles_m * p.tiles_n;

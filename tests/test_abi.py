@@ -208,10 +208,15 @@ def test_dequant_batch_rejects(L):
 
 
 def test_workspace_planning(L):
-    # k/v projection at M=2048 underfills 256 CUs with 256x128 tiles -> split
-    ws = L.mq_gemm_workspace_bytes(12, 2048, 512, 3584, 0)
-    assert ws > 0 and ws % (2048 * 512 * 4) == 0
-    assert L.mq_gemm_workspace_bytes(0, 2048, 512, 3584, 0) == ws
+    # k/v projection at M=2048 underfills 256 CUs with 256x128 tiles -> split:
+    # the cache GEMM takes 64-row tiles (128 of them, split 2 ways), the fused
+    # one 128-row tiles (64, split 4 ways: each weight decoded 16 times, not 32)
+    assert L.mq_gemm_workspace_bytes(0, 2048, 512, 3584, 0) == 2 * 128 * 64 * 128 * 4
+    for fmt in (8, 12, 14):
+        assert L.mq_gemm_workspace_bytes(fmt, 2048, 512, 3584, 0) == 4 * 64 * 128 * 128 * 4
+    # with fewer than 64 tiles of 128 rows the fused GEMM keeps 64-row tiles
+    assert L.mq_gemm_workspace_bytes(12, 1024, 512, 3584, 0) == \
+        L.mq_gemm_workspace_bytes(0, 1024, 512, 3584, 0)
     # gate/up: 8 x 74 tiles of 256 x 256 = two full rounds of 256 plus 80 tiles,
     # which are split 256 // 80 = 3 ways along K
     assert L.mq_gemm_workspace_bytes(0, 2048, 18944, 3584, 0) == 3 * 80 * 256 * 256 * 4
@@ -247,7 +252,8 @@ def test_workspace_planning(L):
     x16 = 2048 * 3584 * 2
     for fmt in (0, 2, 12, 13, 14):
         assert L.mq_gemm_xf32_workspace_bytes(fmt, 2048, 18944, 3584, 0) == x16 + 3 * 80 * 256 * 256 * 4
-    assert L.mq_gemm_xf32_workspace_bytes(12, 2048, 512, 3584, 0) == x16 + ws
+    assert L.mq_gemm_xf32_workspace_bytes(12, 2048, 512, 3584, 0) == \
+        x16 + L.mq_gemm_workspace_bytes(12, 2048, 512, 3584, 0)
     # padded row stride for the converted X when 2K bytes is a multiple of 2048;
     # 65 rows of 4160 halves = 540800 bytes, rounded up to 540928
     assert L.mq_gemm_xf32_workspace_bytes(0, 65, 4096, 4096, 1) == 540928

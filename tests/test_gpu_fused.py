@@ -69,6 +69,22 @@ def test_eight_wave_tiles_integer_exact(fmt, M, N, K, split):
     assert np.array_equal(Y[rows].astype(np.float64), Yref)
 
 
+@pytest.mark.parametrize("fmt", [8, 12, 14])
+@pytest.mark.parametrize("M,N,K", [(2048, 512, 3584), (2011, 900, 2048), (1024, 512, 3584)])
+def test_narrow_output_tiles_integer_exact(fmt, M, N, K):
+    """Narrow outputs take 128-row tiles in the fused GEMM while 64 or more of
+    them exist (k/v at M = 2048: 64 tiles split 4 ways; M = 2011, N = 900:
+    ragged, 16 x 8 tiles split 2 ways), else 64-row tiles as the cache GEMM
+    does (M = 1024).  Integer inputs: every sampled element exact."""
+    q = synth.weights(fmt, synth.rng(40, 0, fmt, N), N, K, mode="integer")
+    x = synth.activations(synth.rng(40, role=1), M, K, mode="integer")
+    Y = to_host(_fused(fmt, x, q, N, K))
+    edges = np.array([0, 63, 64, 127, 128, 255, 256, M - 1])
+    rows = np.unique(np.concatenate([edges[edges < M], np.random.default_rng(40).choice(M, 12)]))
+    Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(fmt, q, N, K))
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
+
+
 @pytest.mark.parametrize("fmt", [12, 8])
 def test_large_tile_mixed_grid_integer_exact(fmt):
     """Q4_K and Q8_0 take the 256 x 256 tile once a full round of such tiles
