@@ -301,14 +301,20 @@ __device__ __forceinline__ void load5(__amdgpu_buffer_rsrc_t rs, uint32_t o, uin
     w[4] = buf_load4(rs, a + 16);
 }
 
-// Q6_K: 4 elements (bytes of q) of one dword, value (d·s)·(q − 32).
+// Q6_K: the 8 elements (bytes of q) of two dwords, value (d·s)·(q − 32).
+// ds = d·s has at most 18 significant bits, so q·ds (q < 64) and 32·ds are
+// exact in f32 and one fma gives the exact (q − 32)·ds, as the decode's
+// subtract-then-multiply does, in one instruction less.  Only an exact zero
+// may differ in sign (+0 here where the decode keeps −0 for ds < 0); these
+// values feed only MFMAs, whose sums start at +0, so Y is the same.
 __device__ __forceinline__ u32x4 q6k_chunk(uint32_t q0, uint32_t q1, float ds) {
     q0 = opaque(q0);
     q1 = opaque(q1);
-    return pack8(ds * (ubyte_f32<0>(q0) - 32.0f), ds * (ubyte_f32<1>(q0) - 32.0f),
-                 ds * (ubyte_f32<2>(q0) - 32.0f), ds * (ubyte_f32<3>(q0) - 32.0f),
-                 ds * (ubyte_f32<0>(q1) - 32.0f), ds * (ubyte_f32<1>(q1) - 32.0f),
-                 ds * (ubyte_f32<2>(q1) - 32.0f), ds * (ubyte_f32<3>(q1) - 32.0f));
+    const float c = -32.0f * ds;
+    return pack8(__builtin_fmaf(ds, ubyte_f32<0>(q0), c), __builtin_fmaf(ds, ubyte_f32<1>(q0), c),
+                 __builtin_fmaf(ds, ubyte_f32<2>(q0), c), __builtin_fmaf(ds, ubyte_f32<3>(q0), c),
+                 __builtin_fmaf(ds, ubyte_f32<0>(q1), c), __builtin_fmaf(ds, ubyte_f32<1>(q1), c),
+                 __builtin_fmaf(ds, ubyte_f32<2>(q1), c), __builtin_fmaf(ds, ubyte_f32<3>(q1), c));
 }
 
 // ---------------------------------------------------------------------------
