@@ -80,10 +80,11 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
     if (split > k64) split = k64;
     int per = (k64 + split - 1) / split;
     // the fused Q6_K loader pairs k-steps (2j, 2j + 1), and so does the fused
-    // Q8_0 256 × 256 kernel (K a multiple of 256): ranges start even; the
-    // fused Q4_K 256 × 256 kernel stages whole super-blocks (4 steps)
-    const bool pairs = fmt == kFmtQ6_K ||
-                       (fmt == kFmtQ8_0 && p.bm == 256 && p.bn == 256 && K % 256 == 0);
+    // 256 × 256 kernel of the 32-element block formats (K a multiple of 256):
+    // ranges start even; the fused Q4_K 256 × 256 kernel stages whole
+    // super-blocks (4 steps)
+    const bool b32 = fmt == kFmtQ8_0 || fmt == kFmtQ4_0 || fmt == kFmtQ5_0 || fmt == kFmtQ5_1;
+    const bool pairs = fmt == kFmtQ6_K || (b32 && p.bm == 256 && p.bn == 256 && K % 256 == 0);
     if (pairs && (per & 1) && split > 1) ++per;
     if (fmt == kFmtQ4_K && p.bm == 256 && p.bn == 256 && split > 1) per = (per + 3) / 4 * 4;
     split = (k64 + per - 1) / per;   // no empty range

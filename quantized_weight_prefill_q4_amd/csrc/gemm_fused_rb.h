@@ -1,5 +1,6 @@
-// Fused GEMM kernels that expand Q4_K / Q6_K / Q8_0 weights straight into
-// the MFMA operand registers (256 × 256 tiles).  Included by gemm_kernel.h,
+// Fused GEMM kernels that expand Q4_K / Q6_K and the 32-element block
+// formats' weights straight into the MFMA operand registers (256 × 256
+// tiles).  Included by gemm_kernel.h,
 // whose helpers (loaders, swizzle, tile mapping, store_tile) they use.
 //
 // minfer "05 · 8p — Persistent f16 weight cache + fused dequant-in-GEMM" §2
@@ -547,93 +548,148 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
 
 
 // ---------------------------------------------------------------------------
-// Fused Q8_0 GEMM on 256 × 256 tiles, expanded in the MFMA operand registers
-// (the layout of gemm_q6k_rb_kernel).  For K a multiple of 256 only: a row is
-// then K/256 runs of 8 blocks of 272 bytes, so every row starts on a 16-byte
-// boundary.
+// Fused GEMM for the 32-element block formats (Q8_0, Q4_0, Q5_0, Q5_1) on
+// 256 × 256 tiles, expanded in the MFMA operand registers (the layout of
+// gemm_q6k_rb_kernel).  For K a multiple of 256 only: a row is then K/256
+// runs of 8 blocks (272, 144, 176 or 192 bytes), so every row starts on a
+// 16-byte boundary.
 //
-// The 2×2 loader reads each lane's 34-byte block as three loads (16 + 16 + 4
-// aligned bytes), and every one of them touches the 1-2 lines of 32 rows: the
-// L1 sees each line three times.  Here the unit staged in LDS is half a run
-// (4 blocks, 136 bytes, two k-steps): the 9 aligned 16-byte chunks that cover
-// it (a half starts 8 bytes into a chunk when it is odd), loaded once each,
-// consecutive threads on consecutive chunks of a row.  Thread t stages chunks
-// c = t + 256i (i < 9) of the tile's 256 × 9, row c / 9, chunk c mod 9, at
-// LDS position c: rows are 144 bytes apart, which spreads the 32 rows a lane
-// group reads over 16 bank groups.
+// The 2×2 loaders read each lane's block as two or three loads (16 + 4 [+ 4]
+// or 16 + 16 + 4 aligned bytes), and every one of them touches the 1-2 lines
+// of 32 rows: the L1 sees each line two or three times.  Here the unit staged
+// in LDS is half a run (4 blocks, two k-steps): the CH aligned 16-byte chunks
+// that cover it (a half of 136, 72 or 88 bytes starts 8 bytes into a chunk
+// when it is odd), loaded once each, consecutive threads on consecutive
+// chunks of a row.  Thread t stages chunks c = t + 256i (i < CH) of the
+// tile's 256 × CH, row c / CH, chunk c mod CH, at LDS chunk S·row + chunk mod
+// the odd stride S, which spreads the 32 rows a lane group reads over 16
+// bank groups.
 //
 // Lane l of wave w feeds weight rows 64w + 32f + (l & 31) at k = 16kk +
 // 8(l >> 5) + 0..7 of k-slice kk.  Within step C2 of the half these are
-// block b = 2C2 + kk/2, bytes 2 + 16(kk & 1) + 8(l >> 5) + 0..7, with the
-// block's d in its bytes 0-1.  Block b starts at byte 34b + o of the staged
-// row (o = 8 for odd halves), so the 8 bytes are 2 bytes past a dword for
-// even b (three dwords, realigned) and dword-aligned for odd b.  Value d·q in
-// f32, rounded once to f16, as the decode (q80_chunk).
+// block b = 2C2 + kk/2, elements e0 = 16(kk & 1) + 8(l >> 5) + 0..7: for
+// Q8_0 the int8 bytes 2 + e0.., else the nibbles of bytes (e0 & 15).. (low
+// for kk even) with, for Q5_0 / Q5_1, bits e0.. of qh as the 16s bits.  Block
+// b starts at byte BB·b + o of the staged row (o = 8 for odd Q8_0 / Q4_0 /
+// Q5_0 halves), so each field sits at a byte offset known at compile time up
+// to whole dwords, and is read as one dword or two realigned by 2 bytes.
+// Values: Q8_0 d·q (q80_chunk); Q4_0 / Q5_0 d·(q − 8 / 16) as one fma of
+// d·q and −8d / −16d, Q5_1 fma(d, q, m): the decode's f32 values (d·q and the
+// constant are exact), rounded once to f16.
 //
 // Pipeline as gemm_q6k_rb_kernel: two half buffers; during the two k-steps
-// of half hx the 9 chunks per thread of half hx + 1 are loaded (5, then 4,
-// one step ahead in a register set) and written to the other buffer, last
-// read in half hx − 1.  K ranges start on even steps.
+// of half hx the CH chunks per thread of half hx + 1 are loaded (P0, then
+// CH − P0, one step ahead in a register set) and written to the other
+// buffer, last read in half hx − 1.  K ranges start on even steps.
 // ---------------------------------------------------------------------------
-constexpr int kR8Stride = 9;                             // LDS chunks per row
-constexpr int kR8PerThread = 256 * kR8Stride / kThreads;  // 9
-static_assert(kR8PerThread * kThreads == 256 * kR8Stride, "chunks per thread");
-
-// Chunks [lo, hi) of the thread's 9 belong to part c (5 + 4).
-template <int C>
-struct R8Part {
-    static constexpr int lo = C == 0 ? 0 : 5, hi = C == 0 ? 5 : kR8PerThread;
+template <int FMT>
+struct B32Rb;
+template <>
+struct B32Rb<kFmtQ8_0> {
+    static constexpr int BB = 34, CH = 9, S = 9, P0 = 5, QS = 2, QH = 0;
 };
+template <>
+struct B32Rb<kFmtQ4_0> {
+    static constexpr int BB = 18, CH = 5, S = 5, P0 = 3, QS = 2, QH = 0;
+};
+template <>
+struct B32Rb<kFmtQ5_0> {
+    static constexpr int BB = 22, CH = 6, S = 7, P0 = 3, QS = 6, QH = 2;
+};
+template <>
+struct B32Rb<kFmtQ5_1> {
+    static constexpr int BB = 24, CH = 6, S = 7, P0 = 3, QS = 8, QH = 4;
+};
+
+// Chunks [lo, hi) of the thread's CH belong to part c.
+template <int FMT, int C>
+struct B32Part {
+    static constexpr int lo = C == 0 ? 0 : B32Rb<FMT>::P0;
+    static constexpr int hi = C == 0 ? B32Rb<FMT>::P0 : B32Rb<FMT>::CH;
+};
+
+// The 4 bytes at byte offset OFF (even) of a dword-aligned row.
+template <int OFF>
+__device__ __forceinline__ uint32_t rd32(const uint32_t *rw) {
+    static_assert(OFF % 2 == 0, "fields are 2-byte aligned");
+    if constexpr (OFF % 4 == 0) return rw[OFF / 4];
+    else return __builtin_amdgcn_alignbyte(rw[OFF / 4 + 1], rw[OFF / 4], 2);
+}
 
 // The lane's quant dwords of one k-step for its two weight rows (per
-// k-slice) and the two blocks' d.
-struct R8Raw {
+// k-slice: bytes for Q8_0, 5- or 4-bit values in bytes otherwise) and the
+// two blocks' d and additive constant.
+struct B32Raw {
     uint32_t q[2][4][2];
-    float d[2][2];
+    float d[2][2], c[2][2];
 };
 
-// o4: the staged row's first block at dword o4 (0, or 2 for odd halves).
-template <int C2>
-__device__ __forceinline__ void r8_fetch(const u32x4 *Bc, int o4, int lane, int wave, R8Raw &r) {
+// o4: the staged row's first block at dword o4 (0, or 2 for odd halves of
+// Q8_0, Q4_0 and Q5_0).
+template <int FMT, int C2>
+__device__ __forceinline__ void b32_fetch(const u32x4 *Bc, int o4, int lane, int wave, B32Raw &r) {
+    using G = B32Rb<FMT>;
     const int hl = lane >> 5;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const uint32_t *rw =
-            reinterpret_cast<const uint32_t *>(Bc + (wave * 64 + f * 32 + (lane & 31)) * kR8Stride) +
-            o4;
-        // block 2C2 (even): d at byte 68C2, quants from byte 68C2 + 2
-        constexpr int be = 17 * C2;   // its first dword
-        // block 2C2 + 1 (odd): d at byte 68C2 + 34 (dword be + 8, upper half),
-        // quants from byte 68C2 + 36 (dword be + 9)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const uint32_t *w = rw + be + 4 * kk + 2 * hl;
-            const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
-            r.q[f][kk][0] = __builtin_amdgcn_alignbyte(w1, w0, 2);
-            r.q[f][kk][1] = __builtin_amdgcn_alignbyte(w2, w1, 2);
-        }
-#pragma unroll
-        for (int kk = 2; kk < 4; ++kk) {
-            const uint32_t *w = rw + be + 9 + 4 * (kk - 2) + 2 * hl;
-            r.q[f][kk][0] = w[0];
-            r.q[f][kk][1] = w[1];
-        }
-        r.d[f][0] = f16_bits_to_f32(rw[be]);
-        r.d[f][1] = f16_bits_to_f32(rw[be + 8] >> 16);
+            reinterpret_cast<const uint32_t *>(Bc + (wave * 64 + f * 32 + (lane & 31)) * G::S) + o4;
+        const uint32_t *rh = rw + 2 * hl;   // + 8 bytes for the upper half-wave
+        static_for<4>([&](auto KK) MQ_INLINE {
+            constexpr int kk = KK, b0 = G::BB * (2 * C2 + (kk >> 1));
+            if constexpr (FMT == kFmtQ8_0) {
+                constexpr int o = b0 + 2 + 16 * (kk & 1);
+                r.q[f][kk][0] = rd32<o>(rh);
+                r.q[f][kk][1] = rd32<o + 4>(rh);
+            } else {
+                constexpr int o = b0 + G::QS, n4 = 4 * (kk & 1);
+                uint32_t n0 = (rd32<o>(rh) >> n4) & 0x0F0F0F0Fu;
+                uint32_t n1 = (rd32<o + 4>(rh) >> n4) & 0x0F0F0F0Fu;
+                if constexpr (FMT != kFmtQ4_0) {
+                    const uint32_t hb = rd32<b0 + G::QH>(rw) >> (16 * (kk & 1) + 8 * hl);
+                    n0 |= spread4_to_bit4(hb & 15);
+                    n1 |= spread4_to_bit4((hb >> 4) & 15);
+                }
+                r.q[f][kk][0] = n0;
+                r.q[f][kk][1] = n1;
+            }
+        });
+        static_for<2>([&](auto BBc) MQ_INLINE {
+            constexpr int bb = BBc, b0 = G::BB * (2 * C2 + bb);
+            const uint32_t w = rd32<b0>(rw);
+            const float d = f16_bits_to_f32(w);
+            r.d[f][bb] = d;
+            if constexpr (FMT == kFmtQ4_0) r.c[f][bb] = -8.0f * d;
+            else if constexpr (FMT == kFmtQ5_0) r.c[f][bb] = -16.0f * d;
+            else if constexpr (FMT == kFmtQ5_1) r.c[f][bb] = f16_bits_to_f32(w >> 16);
+            else r.c[f][bb] = 0.0f;
+        });
     }
 }
 
-template <int KK>
-__device__ __forceinline__ half8 q80_frag(const R8Raw &r, int f) {
-    return __builtin_bit_cast(half8, q80_chunk(r.q[f][KK][0], r.q[f][KK][1], r.d[f][KK >> 1]));
+template <int FMT, int KK>
+__device__ __forceinline__ half8 b32_frag(const B32Raw &r, int f) {
+    const float d = r.d[f][KK >> 1];
+    if constexpr (FMT == kFmtQ8_0) {
+        return __builtin_bit_cast(half8, q80_chunk(r.q[f][KK][0], r.q[f][KK][1], d));
+    } else {
+        // opaque: the masked bytes stay single v_cvt_f32_ubyteK conversions
+        const uint32_t w0 = opaque(r.q[f][KK][0]), w1 = opaque(r.q[f][KK][1]);
+        const float c = r.c[f][KK >> 1];
+        return __builtin_bit_cast(
+            half8, pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), c), __builtin_fmaf(d, ubyte_f32<1>(w0), c),
+                         __builtin_fmaf(d, ubyte_f32<2>(w0), c), __builtin_fmaf(d, ubyte_f32<3>(w0), c),
+                         __builtin_fmaf(d, ubyte_f32<0>(w1), c), __builtin_fmaf(d, ubyte_f32<1>(w1), c),
+                         __builtin_fmaf(d, ubyte_f32<2>(w1), c), __builtin_fmaf(d, ubyte_f32<3>(w1), c)));
+    }
 }
 
-template <int C2, class Slot>
-__device__ __forceinline__ void rb8_step(const u32x4 *Ac, const u32x4 *Bc, int o4,
+template <int FMT, int C2, class Slot>
+__device__ __forceinline__ void b32_step(const u32x4 *Ac, const u32x4 *Bc, int o4,
                                          f32x16 (&acc)[8][2], int lane, int wave, Slot &&slot) {
     const int hl = lane >> 5;
-    R8Raw raw;
-    r8_fetch<C2>(Bc, o4, lane, wave, raw);
+    B32Raw raw;
+    b32_fetch<FMT, C2>(Bc, o4, lane, wave, raw);
     half8 af[2][8], bf[2][2];
     auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
         constexpr int kk = KKc;
@@ -645,14 +701,14 @@ __device__ __forceinline__ void rb8_step(const u32x4 *Ac, const u32x4 *Bc, int o
         }
     };
     load_a(std::integral_constant<int, 0>(), af[0]);
-    bf[0][0] = q80_frag<0>(raw, 0);
-    bf[0][1] = q80_frag<0>(raw, 1);
+    bf[0][0] = b32_frag<FMT, 0>(raw, 0);
+    bf[0][1] = b32_frag<FMT, 0>(raw, 1);
     static_for<4>([&](auto KK) MQ_INLINE {
         constexpr int kk = KK, c = kk & 1;
         if constexpr (kk + 1 < 4) {
             load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
-            bf[c ^ 1][0] = q80_frag<kk + 1>(raw, 0);
-            bf[c ^ 1][1] = q80_frag<kk + 1>(raw, 1);
+            bf[c ^ 1][0] = b32_frag<FMT, kk + 1>(raw, 0);
+            bf[c ^ 1][1] = b32_frag<FMT, kk + 1>(raw, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         static_for<16>([&](auto IJ) MQ_INLINE {
@@ -669,12 +725,14 @@ __device__ __forceinline__ void rb8_step(const u32x4 *Ac, const u32x4 *Bc, int o
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_q80_rb_kernel(Args a) {
-    static_assert(FMT == kFmtQ8_0, "Q8_0 only");
+__global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
+    using G = B32Rb<FMT>;
     constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
     constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
+    constexpr int HB = 4 * G::BB;                  // bytes of a half run
+    constexpr int OODD = (HB % 16) / 4;            // odd halves: first block at this dword
     __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
-    __shared__ u32x4 Bq0[256 * kR8Stride], Bq1[256 * kR8Stride];
+    __shared__ u32x4 Bq0[256 * G::S], Bq1[256 * G::S];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = 0, wn = wave;
@@ -701,27 +759,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q80_rb_kernel(Args a) {
     la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
     constexpr int NA = decltype(la)::NPART;
     // raw weight chunks (rows 16-byte aligned): chunk c = t + 256i of the
-    // tile's 256 × 9 is row c / 9, chunk c mod 9, LDS position c
+    // tile's 256 × CH is row c / CH, chunk c mod CH, LDS chunk S·row + that
     const int rows_valid = min(BN, a.N - n0);
     const __amdgpu_buffer_rsrc_t rsb =
         make_rsrc(a.W + (int64_t)n0 * a.ldw, (uint32_t)(rows_valid * a.ldw));
     const int t = (int)threadIdx.x;
-    uint32_t roff[kR8PerThread];
+    uint32_t roff[G::CH];
+    int lpos[G::CH];
 #pragma unroll
-    for (int i = 0; i < kR8PerThread; ++i) {
-        const int c = t + kThreads * i, row = c / kR8Stride;
-        roff[i] = (uint32_t)(row * a.ldw) + 16u * (uint32_t)(c - row * kR8Stride);
+    for (int i = 0; i < G::CH; ++i) {
+        const int c = t + kThreads * i, row = c / G::CH, ch = c - row * G::CH;
+        roff[i] = (uint32_t)(row * a.ldw) + 16u * (uint32_t)ch;
+        lpos[i] = row * G::S + ch;
     }
-    u32x4 bv[2][5];
+    constexpr int NSET = G::P0 > G::CH - G::P0 ? G::P0 : G::CH - G::P0;
+    u32x4 bv[2][NSET];
     // load chunk i of half hx into slot (set, j): the half's bytes start at
-    // 136·hx, in the chunk at or below it
+    // HB·hx, in the chunk at or below it
     auto bload = [&](int set, int j, int i, int hx) MQ_INLINE {
-        const uint32_t o = hx < hx_end ? roff[i] + ((136u * (uint32_t)hx) & ~15u) : kOOB;
+        const uint32_t o = hx < hx_end ? roff[i] + (((uint32_t)HB * (uint32_t)hx) & ~15u) : kOOB;
         bv[set][j] = buf_load16(rsb, o);
     };
-    auto bstore = [&](int set, int j, int i, u32x4 *buf) MQ_INLINE {
-        buf[t + kThreads * i] = bv[set][j];
-    };
+    auto bstore = [&](int set, int j, int i, u32x4 *buf) MQ_INLINE { buf[lpos[i]] = bv[set][j]; };
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -738,20 +797,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q80_rb_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.load(0, i);
 #pragma unroll
-        for (int i = 0; i < 5; ++i) bload(0, i, i, hx0);
+        for (int i = 0; i < G::P0; ++i) bload(0, i, i, hx0);
         la.begin(1, k0 + BK, kt_begin + 1 < kt_end);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.load(1, i);
 #pragma unroll
-        for (int i = 0; i < 5; ++i) bstore(0, i, i, B);
+        for (int i = 0; i < G::P0; ++i) bstore(0, i, i, B);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bload(0, i, 5 + i, hx0);
+        for (int i = 0; i < G::CH - G::P0; ++i) bload(0, i, G::P0 + i, hx0);
 #pragma unroll
-        for (int i = 0; i < 5; ++i) bload(1, i, i, hx0 + 1);
+        for (int i = 0; i < G::P0; ++i) bload(1, i, i, hx0 + 1);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.store(0, i, A0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bstore(0, i, 5 + i, B);
+        for (int i = 0; i < G::CH - G::P0; ++i) bstore(0, i, G::P0 + i, B);
         sync_lds();
     }
 
@@ -762,15 +821,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q80_rb_kernel(Args a) {
         constexpr int C2 = decltype(C2c)::value, P = C2;
         constexpr int H = 16;
         constexpr int lpart = 1 - C2;
-        constexpr int NBL = R8Part<lpart>::hi - R8Part<lpart>::lo;
-        constexpr int NBS = R8Part<C2>::hi - R8Part<C2>::lo;
+        constexpr int NBL = B32Part<FMT, lpart>::hi - B32Part<FMT, lpart>::lo;
+        constexpr int NBS = B32Part<FMT, C2>::hi - B32Part<FMT, C2>::lo;
         u32x4 *An = P ? A0 : A1;
         const int hx = kt >> 1;
         const u32x4 *Bc = (hx & 1) ? Bq1 : Bq0;
         u32x4 *Bn = (hx & 1) ? Bq0 : Bq1;
         const int hl_next = C2 == 0 ? hx + 1 : hx + 2;
         la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
-        rb8_step<C2>(P ? A1 : A0, Bc, 2 * (hx & 1), acc, lane, wave, [&](auto SL) MQ_INLINE {
+        b32_step<FMT, C2>(P ? A1 : A0, Bc, OODD * (hx & 1), acc, lane, wave, [&](auto SL) MQ_INLINE {
             constexpr int sl = SL, half = sl < H ? sl : sl - H;
             constexpr int TOT = NA + (sl < H ? NBL : NBS);
             constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
@@ -778,10 +837,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q80_rb_kernel(Args a) {
                 constexpr int o = lo + O;
                 if constexpr (sl < H) {
                     if constexpr (o < NA) la.load(P, o);
-                    else bload(P, o - NA, R8Part<lpart>::lo + (o - NA), hl_next);
+                    else bload(P, o - NA, B32Part<FMT, lpart>::lo + (o - NA), hl_next);
                 } else {
                     if constexpr (o < NA) la.store(1 - P, o, An);
-                    else bstore(1 - P, o - NA, R8Part<C2>::lo + (o - NA), Bn);
+                    else bstore(1 - P, o - NA, B32Part<FMT, C2>::lo + (o - NA), Bn);
                 }
             });
         });

@@ -34,7 +34,8 @@
 // store the f16 tile to LDS: each weight element is expanded once per block
 // tile (⌈M/BM⌉ times in all), not once per wave.  Fused Q4_K and Q6_K on
 // 256 × 256 tiles have kernels of their own (gemm_q4k_rb_kernel,
-// gemm_q6k_rb_kernel, gemm_q80_rb_kernel for K a multiple of 256, below) that
+// gemm_q6k_rb_kernel, gemm_b32_rb_kernel for the 32-element block formats
+// with K a multiple of 256, below) that
 // stage raw (half) super-blocks or block runs in LDS and expand them in the
 // MFMA operand registers.
 
@@ -1011,9 +1012,10 @@ hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t strea
         } else if constexpr (FMT == kFmtQ6_K && !XF32) {
             hipLaunchKernelGGL(gemm_q6k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
             return hipGetLastError();
-        } else if constexpr (FMT == kFmtQ8_0 && !XF32) {
-            if (a.K % 256 == 0) {   // rows of whole 272-byte runs: 16-byte aligned
-                hipLaunchKernelGGL(gemm_q80_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream,
+        } else if constexpr ((FMT == kFmtQ8_0 || FMT == kFmtQ4_0 || FMT == kFmtQ5_0 ||
+                              FMT == kFmtQ5_1) && !XF32) {
+            if (a.K % 256 == 0) {   // rows of whole 8-block runs: 16-byte aligned
+                hipLaunchKernelGGL(gemm_b32_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream,
                                    a);
                 return hipGetLastError();
             }

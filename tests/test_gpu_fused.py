@@ -144,26 +144,28 @@ def test_q6k_large_tile_k_ranges_exact(M, N, K, split):
         assert np.array_equal(Yf1, Yc1)
 
 
+@pytest.mark.parametrize("fmt", [8, 2, 6, 7])
 @pytest.mark.parametrize("M,N,K,split", [(2011, 8348, 2048, 0), (2011, 8348, 2048, 3),
                                          (300, 32768, 1280, 7), (1000, 14336, 768, 0),
                                          (2011, 8348, 1056, 0), (2011, 8348, 1056, 3)])
-def test_q80_large_tile_k_ranges_exact(M, N, K, split):
-    """The Q8_0 256 x 256 kernel for K a multiple of 256 stages half runs of
-    4 blocks (2 k-steps): ragged M and N, the plan's tail, a forced 3-way
-    split of 32 steps (ranges 12, 12, 8), a forced 7-way split of 20 steps
-    (5 ranges of 4), a 3/4 round unsplit with K = 768; with K = 1056 (not a
-    multiple of 256) the 2 x 2 kernel takes the same tiles.  Integer inputs:
-    every sampled element exact, and equal to the cache path at split 1."""
-    q = synth.weights(8, synth.rng(39, 0, 8, N), N, K, mode="integer")
+def test_b32_large_tile_k_ranges_exact(fmt, M, N, K, split):
+    """The 256 x 256 kernel of the 32-element block formats (K a multiple of
+    256) stages half runs of 4 blocks (2 k-steps): ragged M and N, the plan's
+    tail, a forced 3-way split of 32 steps (ranges 12, 12, 8), a forced 7-way
+    split of 20 steps (5 ranges of 4), a 3/4 round unsplit with K = 768; with
+    K = 1056 (not a multiple of 256) the 2 x 2 kernel takes the same tiles.
+    Integer inputs: every sampled element exact, and equal to the cache path
+    at split 1."""
+    q = synth.weights(fmt, synth.rng(39, 0, fmt, N), N, K, mode="integer")
     x = synth.activations(synth.rng(39, role=1), M, K, mode="integer")
-    Y = to_host(_fused(8, x, q, N, K, split_k=split))
+    Y = to_host(_fused(fmt, x, q, N, K, split_k=split))
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(39).choice(M, 12)]))
-    w16 = oracle.dequant_ref(8, q, N, K)
+    w16 = oracle.dequant_ref(fmt, q, N, K)
     Yref, _ = oracle.gemm_ref(x[rows], w16)
     assert np.array_equal(Y[rows].astype(np.float64), Yref)
     if split == 0:
-        Yf1 = to_host(_fused(8, x, q, N, K, split_k=1))
-        announce("gemm_f16cache", "Q8_0 cache", f"M={M} N={N} K={K}", "split=1")
+        Yf1 = to_host(_fused(fmt, x, q, N, K, split_k=1))
+        announce("gemm_f16cache", f"{FMT_NAME[fmt]} cache", f"M={M} N={N} K={K}", "split=1")
         Yc1 = to_host(mq.gemm_f16cache(to_dev_f16(x), to_dev_f16(w16), K, split_k=1))
         assert np.array_equal(Yf1, Yc1)
 
@@ -184,7 +186,7 @@ def _large_tile_cases(seed, n):
     return out
 
 
-@pytest.mark.parametrize("fmt", [8, 12, 14])
+@pytest.mark.parametrize("fmt", [2, 6, 7, 8, 12, 14])
 @pytest.mark.parametrize("M,N,K,split", _large_tile_cases(37, 4))
 def test_register_expansion_kernels_random_shapes_exact(fmt, M, N, K, split):
     q = synth.weights(fmt, synth.rng(37, 0, fmt, N + K), N, K, mode="integer")
