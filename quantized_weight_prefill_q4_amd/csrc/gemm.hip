@@ -82,11 +82,12 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
     // the fused Q6_K loader pairs k-steps (2j, 2j + 1), and so does the fused
     // 256 × 256 kernel of the 32-element block formats (K a multiple of 256):
     // ranges start even; the fused Q4_K 256 × 256 kernel stages whole
-    // super-blocks (4 steps)
+    // super-blocks (4 steps), and so does the fused Q5_K one
     const bool b32 = fmt == kFmtQ8_0 || fmt == kFmtQ4_0 || fmt == kFmtQ5_0 || fmt == kFmtQ5_1;
     const bool pairs = fmt == kFmtQ6_K || (b32 && p.bm == 256 && p.bn == 256 && K % 256 == 0);
     if (pairs && (per & 1) && split > 1) ++per;
-    if (fmt == kFmtQ4_K && p.bm == 256 && p.bn == 256 && split > 1) per = (per + 3) / 4 * 4;
+    if ((fmt == kFmtQ4_K || fmt == kFmtQ5_K) && p.bm == 256 && p.bn == 256 && split > 1)
+        per = (per + 3) / 4 * 4;
     split = (k64 + per - 1) / per;   // no empty range
     if (split == 1) dp = tiles;
     p.dp_tiles = dp;

@@ -53,15 +53,29 @@ namespace {
 // barrier (the fourth quarter writes no part).  K ranges are whole
 // super-blocks.
 // ---------------------------------------------------------------------------
-constexpr int kRbChunks = 256 * 144 / 16;           // 16-byte chunks of a tile super-block
-constexpr int kRbPerThread = kRbChunks / kThreads;  // 9
-static_assert(kRbPerThread * kThreads == kRbChunks, "chunks per thread");
+//
+// Q5_K takes the same kernel: its 176-byte super-blocks (the Q4_K header,
+// then 32 qh bytes, then the 128 quant bytes) are 11 chunks per row, and the
+// lane also reads the 8 qh bytes at the positions of its quant bytes; bit j
+// of qh[l] is the 16s bit of element l of sub-block j.
+// ---------------------------------------------------------------------------
+template <int FMT>
+struct KRb;
+template <>
+struct KRb<kFmtQ4_K> {
+    static constexpr int CH = 9, BB = 144, QSC = 1, PER = 3;   // chunks per row, bytes, qs chunk
+};
+template <>
+struct KRb<kFmtQ5_K> {
+    static constexpr int CH = 11, BB = 176, QSC = 3, PER = 4;
+};
 
-// Chunks [lo, hi) of the thread's 9 belong to part c4 (loaded for step c4).
-template <int C4>
+// Chunks [lo, hi) of the thread's CH belong to part c4 (loaded for step c4).
+template <int FMT, int C4>
 struct RbPart {
-    static constexpr int lo = C4 * 3 < kRbPerThread ? C4 * 3 : kRbPerThread;
-    static constexpr int hi = (C4 + 1) * 3 < kRbPerThread ? (C4 + 1) * 3 : kRbPerThread;
+    static constexpr int n = KRb<FMT>::CH, per = KRb<FMT>::PER;
+    static constexpr int lo = C4 * per < n ? C4 * per : n;
+    static constexpr int hi = (C4 + 1) * per < n ? (C4 + 1) * per : n;
 };
 
 // Scale and min (as the f32 factors d·sc and dmin·m) of sub-blocks 2c4 and
@@ -90,51 +104,65 @@ __device__ __forceinline__ void q4k_sub_scales(const u32x4 h, float &A0, float &
     C1 = dmin * (float)m1;
 }
 
-// The B fragment of k-slice kk from the lane's quant bytes qa (bytes 8h..)
-// and qb (bytes 16 + 8h..) of the quarter.
-template <int KK>
-__device__ __forceinline__ half8 q4k_frag(u32x2 qa, u32x2 qb, float A0, float C0, float A1,
-                                          float C1) {
-    constexpr uint32_t L = 0x0F0F0F0Fu;
-    const u32x2 q = (KK & 1) ? qb : qa;
-    const uint32_t w0 = (KK < 2) ? (q.x & L) : ((q.x >> 4) & L);
-    const uint32_t w1 = (KK < 2) ? (q.y & L) : ((q.y >> 4) & L);
-    return __builtin_bit_cast(half8, q4k_chunk(w0, w1, KK < 2 ? A0 : A1, KK < 2 ? C0 : C1));
-}
-
 // What a lane needs of its two weight rows for one k-step: the quant bytes
-// (qa: bytes 8h.., qb: bytes 16 + 8h.. of the quarter), the two sub-blocks'
-// factors, and the expanded fragments of k-slice 0.  Read and computed during
-// the previous k-step, so a step starts with its first MFMAs.
+// (qa: bytes 8h.., qb: bytes 16 + 8h.. of the quarter), for Q5_K the qh bytes
+// at the same positions shifted right by 2c4 (bit 0 of each byte: sub-block
+// 2c4, bit 1: 2c4 + 1), the two sub-blocks' factors, and the expanded
+// fragments of k-slice 0.  Read and computed during the previous k-step, so a
+// step starts with its first MFMAs.
 struct RbRaw {
-    u32x2 qa[2], qb[2];
+    u32x2 qa[2], qb[2], ha[2], hb[2];
     float A0[2], C0[2], A1[2], C1[2];
     half8 bf0[2];
 };
 
-template <int C4>
+// The B fragment of k-slice kk of weight row f.
+template <int FMT, int KK>
+__device__ __forceinline__ half8 q4k_frag(const RbRaw &r, int f) {
+    constexpr uint32_t L = 0x0F0F0F0Fu, B = 0x01010101u;
+    const u32x2 q = (KK & 1) ? r.qb[f] : r.qa[f];
+    uint32_t w0 = (KK < 2) ? (q.x & L) : ((q.x >> 4) & L);
+    uint32_t w1 = (KK < 2) ? (q.y & L) : ((q.y >> 4) & L);
+    if constexpr (FMT == kFmtQ5_K) {
+        const u32x2 hq = (KK & 1) ? r.hb[f] : r.ha[f];
+        constexpr int j = KK < 2 ? 0 : 1;
+        w0 |= ((hq.x >> j) & B) << 4;
+        w1 |= ((hq.y >> j) & B) << 4;
+    }
+    return __builtin_bit_cast(half8, q4k_chunk(w0, w1, KK < 2 ? r.A0[f] : r.A1[f],
+                                               KK < 2 ? r.C0[f] : r.C1[f]));
+}
+
+template <int FMT, int C4>
 __device__ __forceinline__ void rb_fetch(const u32x4 *Bc, int lane, int wave, RbRaw &r) {
+    using G = KRb<FMT>;
     const int h = lane >> 5;
     u32x4 hdr[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * 9;   // the row's 144 bytes
+        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * G::CH;   // the row's block
         hdr[f] = blk[0];
-        const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk + 1 + 2 * C4);
+        const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk + G::QSC + 2 * C4);
         r.qa[f] = q2[h];
         r.qb[f] = q2[2 + h];
+        if constexpr (FMT == kFmtQ5_K) {
+            const u32x2 *h2 = reinterpret_cast<const u32x2 *>(blk + 1);
+            const u32x2 ha = h2[h], hb = h2[2 + h];
+            r.ha[f] = u32x2{ha.x >> (2 * C4), ha.y >> (2 * C4)};
+            r.hb[f] = u32x2{hb.x >> (2 * C4), hb.y >> (2 * C4)};
+        }
     }
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         q4k_sub_scales<C4>(hdr[f], r.A0[f], r.C0[f], r.A1[f], r.C1[f]);
-        r.bf0[f] = q4k_frag<0>(r.qa[f], r.qb[f], r.A0[f], r.C0[f], r.A1[f], r.C1[f]);
+        r.bf0[f] = q4k_frag<FMT, 0>(r, f);
     }
 }
 
 // One k-step of the wave's 256 × 64 tile from X stage Ac and the raw bytes
 // `cur` (fetched during the previous step); fetches the next step's raw
 // bytes (quarter NC4 of buffer Bnext) into `nxt` between the MFMAs.
-template <int NC4, class Slot>
+template <int FMT, int NC4, class Slot>
 __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32x16 (&acc)[8][2],
                                         int lane, int wave, const RbRaw &cur, RbRaw &nxt,
                                         Slot &&slot) {
@@ -157,11 +185,9 @@ __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32
         if constexpr (kk + 1 < 4) {
             load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
 #pragma unroll
-            for (int f = 0; f < 2; ++f)
-                bf[c ^ 1][f] = q4k_frag<kk + 1>(cur.qa[f], cur.qb[f], cur.A0[f], cur.C0[f],
-                                                cur.A1[f], cur.C1[f]);
+            for (int f = 0; f < 2; ++f) bf[c ^ 1][f] = q4k_frag<FMT, kk + 1>(cur, f);
         } else {
-            rb_fetch<NC4>(Bnext, lane, wave, nxt);
+            rb_fetch<FMT, NC4>(Bnext, lane, wave, nxt);
         }
         __builtin_amdgcn_sched_barrier(0);
         static_for<16>([&](auto IJ) MQ_INLINE {
@@ -179,11 +205,13 @@ __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
-    static_assert(FMT == kFmtQ4_K, "Q4_K only");
+    static_assert(FMT == kFmtQ4_K || FMT == kFmtQ5_K, "Q4_K or Q5_K");
+    using G = KRb<FMT>;
     constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
     constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
+    constexpr int NT = G::CH;   // chunks per thread (256 rows × CH over 256 threads)
     __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
-    __shared__ u32x4 Bq0[kRbChunks], Bq1[kRbChunks];
+    __shared__ u32x4 Bq0[256 * G::CH], Bq1[256 * G::CH];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = 0, wn = wave;
@@ -210,18 +238,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
     F16Loader<BM> la;
     la.init((const uint16_t *)a.X + (int64_t)m0 * a.ldx, min(BM, a.M - m0), a.ldx, a.K);
     constexpr int NA = decltype(la)::NPART;
-    // raw weight chunks: chunk c = thread + 256·i is byte 16(c mod 9) of the
-    // super-block of tile row c / 9, and lands at LDS chunk c
+    // raw weight chunks: chunk c = thread + 256·i is byte 16(c mod CH) of the
+    // super-block of tile row c / CH, and lands at LDS chunk c
     const int rows_valid = min(BN, a.N - n0);
     const __amdgpu_buffer_rsrc_t rsb =
         make_rsrc(a.W + (int64_t)n0 * a.ldw, (uint32_t)(rows_valid * a.ldw));
-    uint32_t goff[kRbPerThread];
+    uint32_t goff[NT];
 #pragma unroll
-    for (int i = 0; i < kRbPerThread; ++i) {
-        const int c = (int)threadIdx.x + kThreads * i, r = c / 9;
-        goff[i] = (uint32_t)(r * a.ldw + 16 * (c - 9 * r));
+    for (int i = 0; i < NT; ++i) {
+        const int c = (int)threadIdx.x + kThreads * i, r = c / G::CH;
+        goff[i] = (uint32_t)(r * a.ldw + 16 * (c - G::CH * r));
     }
-    u32x4 bv[2][3];
+    u32x4 bv[2][G::PER];
     RbRaw raw[2];   // raw bytes of the current and the next k-step (index P, 1 − P)
 
     f32x16 acc[FM][FN];
@@ -235,9 +263,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
     // register set 1
     {
         const int sb0 = kt_begin >> 2, k0 = kt_begin * BK;
-        u32x4 t[kRbPerThread];
+        u32x4 t[NT];
 #pragma unroll
-        for (int i = 0; i < kRbPerThread; ++i) t[i] = buf_load16(rsb, goff[i] + (uint32_t)sb0 * 144u);
+        for (int i = 0; i < NT; ++i) t[i] = buf_load16(rsb, goff[i] + (uint32_t)sb0 * (uint32_t)G::BB);
         la.begin(0, k0, true);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.load(0, i);
@@ -246,15 +274,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
         for (int i = 0; i < NA; ++i) la.load(1, i);
         const bool nlive = sb0 + 1 < sb_end;
 #pragma unroll
-        for (int i = RbPart<0>::lo; i < RbPart<0>::hi; ++i)
-            bv[1][i - RbPart<0>::lo] = buf_load16(rsb, nlive ? goff[i] + (uint32_t)(sb0 + 1) * 144u : kOOB);
+        for (int i = RbPart<FMT, 0>::lo; i < RbPart<FMT, 0>::hi; ++i)
+            bv[1][i - RbPart<FMT, 0>::lo] =
+                buf_load16(rsb, nlive ? goff[i] + (uint32_t)(sb0 + 1) * (uint32_t)G::BB : kOOB);
 #pragma unroll
         for (int i = 0; i < NA; ++i) la.store(0, i, A0);
         u32x4 *B = (sb0 & 1) ? Bq1 : Bq0;
 #pragma unroll
-        for (int i = 0; i < kRbPerThread; ++i) B[threadIdx.x + kThreads * i] = t[i];
+        for (int i = 0; i < NT; ++i) B[threadIdx.x + kThreads * i] = t[i];
         sync_lds();
-        rb_fetch<0>(B, lane, wave, raw[0]);
+        rb_fetch<FMT, 0>(B, lane, wave, raw[0]);
     }
 
     // Step kt (quarter C4, P = C4 & 1): X as in gemm_kernel; raw weights:
@@ -264,7 +293,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
     auto step = [&](auto C4c, int kt) MQ_INLINE {
         constexpr int C4 = decltype(C4c)::value, P = C4 & 1;
         constexpr int LC = (C4 + 1) & 3;
-        constexpr int NL = RbPart<LC>::hi - RbPart<LC>::lo, NS = RbPart<C4>::hi - RbPart<C4>::lo;
+        constexpr int NL = RbPart<FMT, LC>::hi - RbPart<FMT, LC>::lo;
+        constexpr int NS = RbPart<FMT, C4>::hi - RbPart<FMT, C4>::lo;
         constexpr int H = 16;
         u32x4 *An = P ? A0 : A1;
         const int sb = kt >> 2;
@@ -273,12 +303,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
         // the next step's raw bytes: this super-block's buffer, or for the
         // last quarter the next one's, complete since the previous barrier
         // (the last quarter writes no part)
-        static_assert(RbPart<3>::lo == RbPart<3>::hi, "the last quarter writes no part");
+        static_assert(RbPart<FMT, 3>::lo == RbPart<FMT, 3>::hi, "the last quarter writes no part");
         const u32x4 *Bnext = C4 == 3 ? Bn : Bc;
         const int sbl = (kt + 1) / 4 + 1;
-        const uint32_t boff = sbl < sb_end ? (uint32_t)sbl * 144u : kOOB;
+        const uint32_t boff = sbl < sb_end ? (uint32_t)sbl * (uint32_t)G::BB : kOOB;
         la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
-        rb_step<(C4 + 1) & 3>(P ? A1 : A0, Bnext, acc, lane, wave, raw[P], raw[1 - P],
+        rb_step<FMT, (C4 + 1) & 3>(P ? A1 : A0, Bnext, acc, lane, wave, raw[P], raw[1 - P],
                               [&](auto SL) MQ_INLINE {
             constexpr int sl = SL, half = sl < H ? sl : sl - H;
             constexpr int TOT = sl < H ? NA + NL : NA + NS;
@@ -288,10 +318,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
                 if constexpr (sl < H) {
                     if constexpr (o < NA) la.load(P, o);
                     else bv[P][o - NA] = buf_load16(
-                        rsb, boff == kOOB ? kOOB : goff[RbPart<LC>::lo + o - NA] + boff);
+                        rsb, boff == kOOB ? kOOB : goff[RbPart<FMT, LC>::lo + o - NA] + boff);
                 } else {
                     if constexpr (o < NA) la.store(1 - P, o, An);
-                    else Bn[threadIdx.x + kThreads * (RbPart<C4>::lo + o - NA)] = bv[1 - P][o - NA];
+                    else Bn[threadIdx.x + kThreads * (RbPart<FMT, C4>::lo + o - NA)] = bv[1 - P][o - NA];
                 }
             });
         });

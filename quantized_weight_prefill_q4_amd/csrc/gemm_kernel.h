@@ -1006,7 +1006,7 @@ hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
 template <int FMT, bool XF32>
 hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t stream) {
     if (bm == 256 && bn == 256) {
-        if constexpr (FMT == kFmtQ4_K && !XF32) {
+        if constexpr ((FMT == kFmtQ4_K || FMT == kFmtQ5_K) && !XF32) {
             hipLaunchKernelGGL(gemm_q4k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
             return hipGetLastError();
         } else if constexpr (FMT == kFmtQ6_K && !XF32) {

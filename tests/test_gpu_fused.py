@@ -101,21 +101,23 @@ def test_large_tile_mixed_grid_integer_exact(fmt):
     assert np.array_equal(Y[rows].astype(np.float64), Yref)
 
 
+@pytest.mark.parametrize("fmt", [12, 13])
 @pytest.mark.parametrize("M,N,K,split", [(2011, 8348, 2048, 0), (2011, 8348, 2048, 3),
                                          (2048, 18944, 3584, 0), (300, 32768, 1280, 3)])
-def test_q4k_large_tile_k_ranges_exact(M, N, K, split):
+def test_q4k_large_tile_k_ranges_exact(fmt, M, N, K, split):
     """The Q4_K 256 x 256 kernel stages whole super-blocks, so its K ranges are
     rounded to multiples of 4 k-steps: a forced 3-way split of 32 steps runs
     ranges of 12, 12 and 8; the 7B gate shape's automatic tail (3 ways over 56
     steps) runs 20, 20, 16; 300 rows over N = 32768 (256 tiles, the second
     M-tile 44 rows deep) split 3 ways over 20 steps runs 8, 8, 4.  Ragged M
     and N (rows of the last tiles past the matrix read as zero weights) and
-    integer inputs: every sampled element exact."""
-    q = synth.weights(12, synth.rng(35, 0, 12, N), N, K, mode="integer")
+    integer inputs: every sampled element exact.  Q5_K (176-byte super-blocks,
+    11 chunks per row) takes the same kernel."""
+    q = synth.weights(fmt, synth.rng(35, 0, fmt, N), N, K, mode="integer")
     x = synth.activations(synth.rng(35, role=1), M, K, mode="integer")
-    Y = to_host(_fused(12, x, q, N, K, split_k=split))
+    Y = to_host(_fused(fmt, x, q, N, K, split_k=split))
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(35).choice(M, 12)]))
-    Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(12, q, N, K))
+    Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(fmt, q, N, K))
     assert np.array_equal(Y[rows].astype(np.float64), Yref)
 
 
@@ -186,7 +188,7 @@ def _large_tile_cases(seed, n):
     return out
 
 
-@pytest.mark.parametrize("fmt", [2, 6, 7, 8, 12, 14])
+@pytest.mark.parametrize("fmt", [2, 6, 7, 8, 12, 13, 14])
 @pytest.mark.parametrize("M,N,K,split", _large_tile_cases(37, 4))
 def test_register_expansion_kernels_random_shapes_exact(fmt, M, N, K, split):
     q = synth.weights(fmt, synth.rng(37, 0, fmt, N + K), N, K, mode="integer")
