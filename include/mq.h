@@ -157,8 +157,10 @@ int mq_dequant_to_f16_batch(const mq_dequant_job *jobs, int n, void *stream);
  * whole rounds of 256 tiles over all of K and splits only the tiles of a last,
  * partial round; a forced split_k >= 2 splits every tile into at most split_k
  * ranges of whole 64-wide k-steps (fewer when ranges must be longer: the
- * fused Q6_K kernel starts ranges on even steps, the fused Q4_K kernel on
- * 256 × 256 tiles on super-block boundaries, i.e. multiples of 4 steps).
+ * fused Q6_K kernel, and on 256 × 256 tiles with K a multiple of 256 the
+ * fused Q8_0 / Q4_0 / Q5_0 / Q5_1 kernel, start ranges on even steps; the
+ * fused Q4_K and Q5_K kernels on 256 × 256 tiles on super-block boundaries,
+ * i.e. multiples of 4 steps).
  *   fmt     : 0 for mq_gemm_f16cache, else the weight format of mq_gemm_fused.
  *   split_k : 0 = let the library choose (as the GEMM will with the same
  *             arguments), 1 = no split, 2..MQ_MAX_SPLIT_K = forced.
