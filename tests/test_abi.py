@@ -232,6 +232,14 @@ def test_workspace_planning(L):
     assert L.mq_gemm_workspace_bytes(12, 300, 32768, 1280, 7) == 5 * 256 * 256 * 256 * 4
     assert L.mq_gemm_workspace_bytes(8, 300, 32768, 1280, 7) == 5 * 256 * 256 * 256 * 4
     assert L.mq_gemm_workspace_bytes(8, 300, 32768, 1056, 7) == 6 * 256 * 256 * 256 * 4
+    # Q5_K takes the Q4_K kernel (ranges of whole super-blocks); Q4_0, Q5_0
+    # and Q5_1 the Q8_0 one (even starts): 20 steps forced 7 ways -> 5 of 4
+    for fmt in (2, 6, 7, 13):
+        assert L.mq_gemm_workspace_bytes(fmt, 300, 32768, 1280, 7) == 5 * 256 * 256 * 256 * 4
+    # 32 steps forced 3 ways: 11-step ranges become 12 (even) or 12 (whole
+    # super-blocks); 3 ranges either way
+    for fmt in (2, 8, 13):
+        assert L.mq_gemm_workspace_bytes(fmt, 300, 32768, 2048, 3) == 3 * 256 * 256 * 256 * 4
     assert L.mq_gemm_workspace_bytes(12, 300, 32768, 1280, 3) == 3 * 256 * 256 * 256 * 4
     # 4096 x 14336 at M = 1024: 64 tiles of 256 x 256 split 4 ways (ranges of
     # 3584 k fill the compute units); at M = 512 the ranges would be 1792 k, so
