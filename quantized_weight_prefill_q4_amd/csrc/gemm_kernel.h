@@ -570,19 +570,24 @@ struct Q32Loader {
             if constexpr (FMT == kFmtQ4_0) {
                 w0 = opaque(w0);
                 w1 = opaque(w1);
-                v = pack8(d * (ubyte_f32<0>(w0) - 8.0f), d * (ubyte_f32<1>(w0) - 8.0f),
-                          d * (ubyte_f32<2>(w0) - 8.0f), d * (ubyte_f32<3>(w0) - 8.0f),
-                          d * (ubyte_f32<0>(w1) - 8.0f), d * (ubyte_f32<1>(w1) - 8.0f),
-                          d * (ubyte_f32<2>(w1) - 8.0f), d * (ubyte_f32<3>(w1) - 8.0f));
+                // d·q and 8d / 16d are exact in f32: one fma gives the
+                // decode's exact d·(q − 8) (only an exact zero's sign may
+                // differ, which the MFMA sums starting at +0 do not see)
+                const float c = -8.0f * d;
+                v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), c), __builtin_fmaf(d, ubyte_f32<1>(w0), c),
+                          __builtin_fmaf(d, ubyte_f32<2>(w0), c), __builtin_fmaf(d, ubyte_f32<3>(w0), c),
+                          __builtin_fmaf(d, ubyte_f32<0>(w1), c), __builtin_fmaf(d, ubyte_f32<1>(w1), c),
+                          __builtin_fmaf(d, ubyte_f32<2>(w1), c), __builtin_fmaf(d, ubyte_f32<3>(w1), c));
             } else {
                 const uint32_t hb = qh >> (8 * c);
                 w0 = opaque(w0 | spread4_to_bit4(hb & 15));
                 w1 = opaque(w1 | spread4_to_bit4((hb >> 4) & 15));
                 if constexpr (FMT == kFmtQ5_0) {
-                    v = pack8(d * (ubyte_f32<0>(w0) - 16.0f), d * (ubyte_f32<1>(w0) - 16.0f),
-                              d * (ubyte_f32<2>(w0) - 16.0f), d * (ubyte_f32<3>(w0) - 16.0f),
-                              d * (ubyte_f32<0>(w1) - 16.0f), d * (ubyte_f32<1>(w1) - 16.0f),
-                              d * (ubyte_f32<2>(w1) - 16.0f), d * (ubyte_f32<3>(w1) - 16.0f));
+                    const float c = -16.0f * d;
+                    v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), c), __builtin_fmaf(d, ubyte_f32<1>(w0), c),
+                              __builtin_fmaf(d, ubyte_f32<2>(w0), c), __builtin_fmaf(d, ubyte_f32<3>(w0), c),
+                              __builtin_fmaf(d, ubyte_f32<0>(w1), c), __builtin_fmaf(d, ubyte_f32<1>(w1), c),
+                              __builtin_fmaf(d, ubyte_f32<2>(w1), c), __builtin_fmaf(d, ubyte_f32<3>(w1), c));
                 } else {
                     const float m = f16_bits_to_f32(h0 >> 16);
                     v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), m), __builtin_fmaf(d, ubyte_f32<1>(w0), m),
