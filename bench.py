@@ -84,6 +84,9 @@ def parse():
                    help="profiling aid: run only this 7B matrix's fused GEMM --steps times")
     p.add_argument("--only-mmq", default=None,
                    help="time only this 7B shape on the int8 path (for counter runs)")
+    p.add_argument("--only-sweep", action="store_true",
+                   help="only the fused-vs-cache sweep (for a kernel trace of its calls); "
+                        "prints its JSON")
     p.add_argument("--only-load", action="store_true",
                    help="profiling aid: run only the batched decode of the 7B weight set --steps times")
     p.add_argument("--calib-copy", action="store_true",
@@ -274,9 +277,9 @@ def forward_fused(mq, W, xa, xf, ys, ws):
 
 
 def sweep(torch, mq, dev, log_rows):
-    """Fused vs cache GEMM time per (shape, M); rotates weight copies over > 512 MB.
-    When the crossover falls between two sweep points, the refinement points
-    between them are measured too."""
+    """Fused vs cache GEMM time per (shape, M), GPU time from graph replays
+    (graph_us) of 12 calls that rotate weight copies over > 512 MB; every M of
+    the sweep and of its refinement list is measured."""
     out = {}
     for si, (name, fmt, N, K) in enumerate(synth.SWEEP_8B):
         q0 = synth.weights_device(fmt, 5000 + si, N, K, dev)
@@ -293,21 +296,13 @@ def sweep(torch, mq, dev, log_rows):
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             ws_c = torch.empty(max(1, mq.workspace_bytes(0, M, N, K) // 4), dtype=torch.float32, device=dev)
             ws_f = torch.empty(max(1, mq.workspace_bytes(fmt, M, N, K) // 4), dtype=torch.float32, device=dev)
-            t = {}
-            for path in ("cache", "fused"):
-                reps = 12
-                evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-                for r in range(reps + 2):                  # 2 warm-up calls
-                    if r >= 2:
-                        evs[r - 2].record()
-                    if path == "cache":
-                        mq.gemm_f16cache(xm, caches[r % nc], K, out=y, ws=ws_c)
-                    else:
-                        mq.gemm_fused(xm, qs[r % nq], fmt, N, K, out=y, ws=ws_f)
-                evs[reps].record()
-                torch.cuda.synchronize()
-                d = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(reps)]
-                t[path] = statistics.median(d)
+            reps = 12
+            t = {
+                "cache": graph_us(torch, [lambda r=r: mq.gemm_f16cache(xm, caches[r % nc], K, out=y, ws=ws_c)
+                                          for r in range(reps)], check=lambda: y.clone()),
+                "fused": graph_us(torch, [lambda r=r: mq.gemm_fused(xm, qs[r % nq], fmt, N, K, out=y, ws=ws_f)
+                                          for r in range(reps)], check=lambda: y.clone()),
+            }
             flops = 2.0 * M * N * K
             res[M] = {"cache_us": round(t["cache"], 2), "fused_us": round(t["fused"], 2),
                       "cache_tflops": round(flops / t["cache"] / 1e6, 1),
@@ -319,35 +314,76 @@ def sweep(torch, mq, dev, log_rows):
             ms = sorted(res)
             wins = [M for M in ms if res[M]["cache_us"] < res[M]["fused_us"]]
             if not wins:
-                return f">{max(ms)}", None
+                return f">{max(ms)}"
             if wins[0] == ms[0]:
-                return f"<={ms[0]}", None
-            return str(wins[0]), (ms[ms.index(wins[0]) - 1], wins[0])
+                return f"<={ms[0]}"
+            return str(wins[0])
 
-        for M in synth.SWEEP_M:
+        for M in sorted(set(synth.SWEEP_M) | set(synth.SWEEP_REFINE)):
             measure(M)
-        cross, between = crossover()
-        if between:
-            for M in synth.SWEEP_REFINE:
-                if between[0] < M < between[1]:
-                    measure(M)
-            cross, _ = crossover()
+        cross = crossover()
         out[name] = {"crossover_M": cross, "by_M": {m: res[m] for m in sorted(res)}}
         del caches, qs, cache0, q0
         torch.cuda.empty_cache()
     return out
 
 
-def _median_us(torch, fn, reps, warm=2):
-    """Median duration (us) of fn(r) over reps calls after warm untimed ones."""
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    for r in range(reps + warm):
-        if r >= warm:
-            evs[r - warm].record()
-        fn(r)
-    evs[reps].record()
+def graph_us(torch, fns, replays=7, check=None):
+    """GPU time per call (us) of the zero-argument calls `fns`, each of which
+    enqueues library work on the current stream: all of them are captured into
+    one HIP graph, which is replayed once untimed and then `replays` times
+    between a pair of HIP events each.  Host launch gaps are not in the time,
+    the GPU's own dispatch between kernels is.  Returns the median over replays
+    of (replay time / len(fns)).  check(): called after an eager run of the
+    calls and again after the timed replays, to confirm the graph computes what
+    the eager calls did (the library records no memset nodes)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    return statistics.median(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(reps))
+    ref = check() if check is not None else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fns:
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(replays)]
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    if check is not None:
+        got = check()
+        if not torch.equal(got, ref):
+            raise RuntimeError("graph replay computed other results than the eager calls")
+    del g
+    return statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3 / len(fns)
+
+
+def _median_us(torch, fn, reps, warm=2):
+    """GPU time per call (us) of fn(r), r = 0 .. reps - 1, from graph replays
+    (graph_us); `warm` is kept for the callers' signature (the graph's first
+    replay is the warm-up)."""
+    return graph_us(torch, [lambda r=r: fn(r) for r in range(reps)])
+
+
+def hbm_copy_gbs(torch, dev, nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of `nbytes` (torch copy_), GB/s counting
+    the bytes read plus the bytes written: the practical HBM ceiling the
+    decode is judged against, measured in the same run."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    us = graph_us(torch, [lambda: dst.copy_(src) for _ in range(reps)])
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / us / 1e3
 
 
 def formats_table(torch, mq, dev, log_rows):
@@ -596,6 +632,106 @@ def grouped_forward(torch, mq, W, xa, xf, steps, dev):
     return statistics.median(d), min(d)
 
 
+FWD_ROWS = 64     # token rows of the timed forward's output sample
+FWD_COLS = 256    # output columns (weight rows) per matrix
+
+
+def forward_sample(torch, W, xa, xf, ys, M):
+    """Host copy of part of what the last timed forward computed: for each of
+    the last layer's seven GEMMs (every call of a shape writes the same output
+    buffer, layer by layer, so the buffers hold layer 27's products),
+    FWD_ROWS token rows x FWD_COLS output columns of Y, the same rows of X,
+    and the quantized bytes and f16-cache rows of the FWD_COLS weight rows.
+    Rows and columns are seeded draws that include the first and the last."""
+    g = np.random.default_rng(7004)
+    rows = np.unique(np.concatenate([[0, M - 1], g.choice(M, FWD_ROWS - 2, replace=False)]))
+    torch.cuda.synchronize()
+    ridx = torch.from_numpy(rows).to(xa.device)
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    out = {"rows": rows, "x": {"a": bits(xa[ridx]), "f": bits(xf[ridx])}, "mats": {}}
+    for name, (fmt, N, K, q, cache) in W[-1].items():
+        cols = np.unique(np.concatenate([[0, N - 1], g.choice(N, FWD_COLS - 2, replace=False)]))
+        cidx = torch.from_numpy(cols).to(xa.device)
+        rb = q.numel() // N
+        out["mats"][name] = {
+            "fmt": fmt, "N": N, "K": K, "cols": cols,
+            "y": ys[name][ridx][:, cidx].cpu().numpy(),
+            "q": q.view(N, rb)[cidx].cpu().numpy(),
+            "cache": bits(cache[cidx, :K]),
+        }
+    return out
+
+
+def check_forward_sample(sample):
+    """The CPU leg's check of the timed forward (untimed): the oracle decodes
+    the sampled weight rows from their quantized bytes (the cache rows must be
+    bit-identical) and computes the sampled outputs in f64 (|dY| <= 1e-3.S +
+    1e-5 per element).  Returns a summary for the JSON line."""
+    import oracle
+
+    worst = max_rel = 0.0
+    cache_ok = True
+    n = 0
+    for name, d in sample["mats"].items():
+        fmt, K, cols = d["fmt"], d["K"], d["cols"]
+        w = oracle.dequant_ref(fmt, d["q"].reshape(-1), len(cols), K)
+        cache_ok &= bool(np.array_equal(w, d["cache"]))
+        x = sample["x"]["f" if name == "down" else "a"]
+        Yref, S = oracle.gemm_ref(x, w, K)
+        ok, r, _, mr = oracle.within_tolerance(d["y"], Yref, S)
+        worst = max(worst, float(r))
+        max_rel = max(max_rel, float(mr))
+        n += d["y"].size
+    return {"gemms": len(sample["mats"]), "layer": "last", "rows": int(len(sample["rows"])),
+            "cols_per_gemm": FWD_COLS, "outputs_checked": n, "cache_bit_exact": cache_ok,
+            "worst_err_over_tolerance": worst, "max_abs_err_over_S": max_rel,
+            "pass": bool(cache_ok and worst <= 1.0)}
+
+
+def fused_grouped_forward(torch, mq, W, xa, xf, steps, dev):
+    """The fused forward with the shared-input weights grouped: per layer the
+    quantized q, k and v rows (all Q4_K over K = 3584) copied into one
+    4608-row weight, gate and up into one 37888-row weight, then four fused
+    GEMMs per layer instead of seven (Fucina "Eager GPU Offload Without A
+    Compute Graph", quantized linears: a shared-input batch).  Returns
+    (median ms per step, min ms per step)."""
+    M = xa.shape[0]
+    groups = []
+    for row in W:
+        qkv = torch.cat([row[n][3] for n in ("q", "k", "v")])
+        gu = torch.cat([row[n][3] for n in ("gate", "up")])
+        groups.append((qkv, row["o"], gu, row["down"]))
+    y_qkv = torch.empty((M, 4608), dtype=torch.float32, device=dev)
+    y_o = torch.empty((M, 3584), dtype=torch.float32, device=dev)
+    y_gu = torch.empty((M, 37888), dtype=torch.float32, device=dev)
+    y_d = torch.empty((M, 3584), dtype=torch.float32, device=dev)
+    q4k, q6k = mq.FORMATS["q4_k"], mq.FORMATS["q6_k"]
+    wsb = max(mq.workspace_bytes(q4k, M, 4608, 3584), mq.workspace_bytes(q4k, M, 3584, 3584),
+              mq.workspace_bytes(q4k, M, 37888, 3584), mq.workspace_bytes(q6k, M, 3584, 18944))
+    ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
+
+    def step():
+        for qkv, o, gu, down in groups:
+            mq.gemm_fused(xa, qkv, q4k, 4608, 3584, out=y_qkv, ws=ws)
+            mq.gemm_fused(xa, o[3], o[0], 3584, 3584, out=y_o, ws=ws)
+            mq.gemm_fused(xa, gu, q4k, 37888, 3584, out=y_gu, ws=ws)
+            mq.gemm_fused(xf, down[3], down[0], 3584, 18944, out=y_d, ws=ws)
+
+    step()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        evs[i].record()
+        step()
+    evs[steps].record()
+    torch.cuda.synchronize()
+    d = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    del groups
+    return statistics.median(d), min(d)
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
@@ -689,6 +825,47 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def _decode_shard(job):
+    """Worker of the row-sharded oracle decode (a separate process): decode the
+    given rows of one weight; returns (seconds, sum of the f16 bit patterns)."""
+    import oracle
+
+    fmt, qrows, n, K = job
+    t0 = time.perf_counter()
+    w = oracle.dequant_ref(fmt, qrows, n, K)
+    return time.perf_counter() - t0, int(w.sum(dtype=np.int64))
+
+
+def _noop(i):
+    return i
+
+
+def parallel_decode(mats, procs):
+    """The oracle decode of `mats` [(fmt, q [N, row_bytes], N, K)], rows sharded
+    over `procs` worker processes (started fresh, warmed before the clock
+    starts).  Returns (wall seconds, per-matrix checksums)."""
+    import concurrent.futures
+    import multiprocessing
+
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=procs, mp_context=ctx) as pool:
+        list(pool.map(_noop, range(4 * procs)))
+        jobs, owner = [], []
+        for mi, (fmt, q, N, K) in enumerate(mats):
+            step = -(-N // procs)
+            for r0 in range(0, N, step):
+                r1 = min(N, r0 + step)
+                jobs.append((fmt, np.ascontiguousarray(q[r0:r1]), r1 - r0, K))
+                owner.append(mi)
+        t0 = time.perf_counter()
+        res = list(pool.map(_decode_shard, jobs))
+        wall = time.perf_counter() - t0
+    sums = [0] * len(mats)
+    for (_, cs), mi in zip(res, owner):
+        sums[mi] += cs
+    return wall, sums
+
+
 def cpu_baseline(rows: int, n_layers: int):
     import oracle
 
@@ -701,6 +878,7 @@ def cpu_baseline(rows: int, n_layers: int):
     t_deq = t_gemm = t_blas = 0.0
     deq_bytes = 0
     flops = 0.0
+    mats, sums = [], []
     for li, mi in ((li, mi) for li in range(n_layers) for mi in range(len(synth.LAYER_7B))):
         name, fmt, N, K = synth.LAYER_7B[mi]
         q = synth.weights(fmt, synth.rng(5, li, mi, 0), N, K)
@@ -708,6 +886,9 @@ def cpu_baseline(rows: int, n_layers: int):
         t0 = time.perf_counter()
         w16 = oracle.dequant_ref(fmt, q, N, K)
         t1 = time.perf_counter()
+        if li == 0:
+            mats.append((fmt, q.reshape(N, -1), N, K))
+            sums.append(int(w16.sum(dtype=np.int64)))
         oracle.gemm_ref(x, w16, K)
         t2 = time.perf_counter()
         # context only: the same product as an f32 BLAS call on the decoded weights
@@ -725,6 +906,13 @@ def cpu_baseline(rows: int, n_layers: int):
     t_gemm /= n_layers
     t_deq /= n_layers
     t_blas /= n_layers
+    # the same decode of one layer's seven weights, rows sharded over the host
+    # cores (at most 16 processes: the machine's CPU share)
+    procs = max(1, min(16, len(os.sched_getaffinity(0))))
+    par_wall, par_sums = parallel_decode(mats, procs)
+    if par_sums != sums:
+        raise RuntimeError("the row-sharded oracle decode disagrees with the single-process one")
+    par_bytes = sum(q.nbytes + 2 * N * K for _, q, N, K in mats)
     return {
         "value": round(rows / (t_gemm * layers), 2),
         "unit": "tok/s",
@@ -737,6 +925,9 @@ def cpu_baseline(rows: int, n_layers: int):
         "gemm_layer_s": round(t_gemm, 3),
         "dequant_gbs": round(deq_bytes / (t_deq * n_layers) / 1e9, 3),
         "dequant_layer_s": round(t_deq, 3),
+        "dequant_parallel_gbs": round(par_bytes / par_wall / 1e9, 3),
+        "dequant_parallel_procs": procs,
+        "dequant_parallel_layer_s": round(par_wall, 3),
         "f32_blas_tflops": round(flops / (t_blas * n_layers) / 1e12, 3),
         "f32_blas_tok_s": round(rows / (t_blas * layers), 2),
     }
@@ -772,6 +963,13 @@ def main():
     if args.only_mmq:
         run_only_mmq(torch, mq, args.only_mmq, args.steps, dev)
         return
+    if args.only_sweep:
+        rows = []
+        cross = sweep(torch, mq, dev, rows)
+        for r in rows:
+            log(r)
+        print(json.dumps({"crossover": cross}), flush=True)
+        return
     if args.only_load:
         W = make_weights(torch, mq, args.layers, dev)
         jobs = [(q, fmt, N, K, cache) for row in W for fmt, N, K, q, cache in row.values()]
@@ -793,6 +991,8 @@ def main():
     cbytes = sum(r[n][1] * r[n][2] * 2 for r in W for n in r)
     log(f"[bench] {layers * 7} weights drawn on device in {time.time() - t0:.1f}s: "
         f"{qbytes / 1e9:.3f} GB quantized, {cbytes / 1e9:.3f} GB f16")
+    copy_gbs = hbm_copy_gbs(torch, dev)
+    log(f"[bench] plain device copy (1 GiB, read + write): {copy_gbs:.0f} GB/s")
     deq_ms, rec = load_phase(torch, mq, W, args.load_reps)
     deq_gbs = (qbytes + cbytes) / (deq_ms / 1e3) / 1e9
     per_fmt = {}
@@ -840,37 +1040,37 @@ def main():
     ev_step_ms = statistics.median(step_ms)
     min_step_ms = min(step_ms)
 
-    # per-call durations (median over steps), per shape and for the roofline
-    # kernel: the instrumented pass
-    steps_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-                    for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        forward(mq, W, xa, xf, ys, ws, events=steps_events[s])
-    torch.cuda.synchronize()
-    inst_step_ms = statistics.median(e[0].elapsed_time(e[-1]) for e in steps_events)
-    per_call = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(calls))]
-                         for e in steps_events])
-    med_call = np.median(per_call, axis=0)
-    flops = np.array([2.0 * M * N * K for _, _, N, K in calls])
+    # What the timed forward computed: a sample of the last layer's seven
+    # outputs (every call of a shape writes the same buffer, layer by layer),
+    # with the rows of X and of the weights it needs, for the oracle check of
+    # the CPU leg.  Untimed.
+    fwd_sample = forward_sample(torch, W, xa, xf, ys, M)
+
+    # Per-call GPU time per shape and of the roofline kernel: graph replays of
+    # the forward's calls of that shape (28 per step; gate and up together for
+    # the roofline), see graph_us.
+    def shape_calls(names):
+        return [lambda fmt=fmt, N=N, K=K, cache=cache, name=name:
+                mq.gemm_f16cache(xf if name == "down" else xa, cache, K, out=ys[name], ws=ws)
+                for row in W for name, (fmt, N, K, q, cache) in row.items() if name in names]
+
     shape_rows = []
     for n, f, N, K in synth.LAYER_7B:
-        idx = [i for i, c in enumerate(calls) if c[0] == n]
-        t_us = float(med_call[idx].mean() * 1e3)
+        t_us = graph_us(torch, shape_calls((n,)), replays=5)
         shape_rows.append((n, N, K, t_us, 2.0 * M * N * K / t_us / 1e6))
-    dom = np.array([i for i, c in enumerate(calls) if c[0] in ROOFLINE_SHAPES])
-    ach = float(flops[dom].sum() / (per_call[:, dom].sum(axis=1).mean() / 1e3) / 1e12)
-    avg_launch_us = float(per_call[:, dom].mean() * 1e3)
+    avg_launch_us = graph_us(torch, shape_calls(ROOFLINE_SHAPES), replays=7)
+    ach = 2.0 * M * 18944 * 3584 / avg_launch_us / 1e6
+    flops = np.array([2.0 * M * N * K for _, _, N, K in calls])
     traffic, traffic_note = measured_traffic()
     gemm_tflops = float(flops.sum() / (ev_step_ms / 1e3) / 1e12)
     tok_s = M * args.steps / wall
     log(f"[bench] forward: {ms_per_step:.3f} ms/step wall, {ev_step_ms:.3f} ms in events, "
-        f"{tok_s:.0f} matmul tok/s, {gemm_tflops:.0f} TFLOP/s over {len(calls)} GEMMs "
-        f"(instrumented pass with an event around every call: {inst_step_ms:.3f} ms/step)")
+        f"{tok_s:.0f} matmul tok/s, {gemm_tflops:.0f} TFLOP/s over {len(calls)} GEMMs; "
+        f"per call (graph replays of each shape's 28 calls):")
     for n, N, K, t_us, tf in shape_rows:
         log(f"    {n:5s} {N:6d}x{K:<6d} {t_us:9.1f} us  {tf:7.1f} TFLOP/s  "
             f"({100 * tf / PEAK_F16_TFLOPS:.1f}% of peak)")
-    log(f"[bench] roofline kernel ({ROOFLINE_KERNEL}, {len(dom)} calls/step): "
+    log(f"[bench] roofline kernel ({ROOFLINE_KERNEL}, {2 * layers} calls/step): "
         f"{ach:.0f} TFLOP/s = {100 * ach / PEAK_F16_TFLOPS:.1f}% of {PEAK_F16_TFLOPS:.0f}, "
         f"avg call {avg_launch_us:.1f} us; traffic {traffic} B/call ({traffic_note})")
 
@@ -930,9 +1130,21 @@ def main():
         b.record()
         torch.cuda.synchronize()
         f_ms = a.elapsed_time(b) / args.fused_steps
+        # element expansions: each weight element once per row tile of its plan
+        expn = sum(-(-M // mq.gemm_plan(f, M, N, K)["bm"]) * N * K for _, f, N, K in calls)
         fused = {"ms_per_step": round(f_ms, 3), "tok_s": round(M / (f_ms / 1e3), 1),
-                 "tflops": round(flops.sum() / (f_ms / 1e3) / 1e12, 1)}
-        log(f"[bench] fused forward: {f_ms:.3f} ms/step, {fused['tok_s']:.0f} tok/s")
+                 "tflops": round(flops.sum() / (f_ms / 1e3) / 1e12, 1),
+                 "expansions_per_step": int(expn),
+                 "expansions_per_s": round(expn / (f_ms / 1e3), 1)}
+        log(f"[bench] fused forward: {f_ms:.3f} ms/step, {fused['tok_s']:.0f} tok/s, "
+            f"{expn / (f_ms / 1e3) / 1e12:.2f} T element expansions/s")
+        if args.grouped_steps > 0:
+            fg_med, fg_min = fused_grouped_forward(torch, mq, W, xa, xf, args.grouped_steps, dev)
+            fused["grouped_ms_per_step_median"] = round(fg_med, 3)
+            fused["grouped_tok_s"] = round(M / (fg_med / 1e3), 1)
+            log(f"[bench] fused grouped forward (4 GEMMs per layer): {fg_med:.3f} ms/step median, "
+                f"{fused['grouped_tok_s']:.0f} tok/s")
+            torch.cuda.empty_cache()
 
     # -- crossover sweep -------------------------------------------------------------
     cross = None
@@ -966,8 +1178,14 @@ def main():
             log(r)
 
     # -- CPU oracle baseline -------------------------------------------------------------
-    cpu = None
+    cpu = fwd_check = None
     if not args.no_cpu:
+        t0 = time.time()
+        fwd_check = check_forward_sample(fwd_sample)
+        log(f"[bench] oracle check of the timed forward ({fwd_check['outputs_checked']} outputs of "
+            f"{fwd_check['gemms']} GEMMs): cache bit-exact {fwd_check['cache_bit_exact']}, worst "
+            f"error {fwd_check['worst_err_over_tolerance']:.2e} of the tolerance "
+            f"({time.time() - t0:.1f}s)")
         t0 = time.time()
         cpu = cpu_baseline(args.cpu_rows, args.cpu_layers)
         log(f"[bench] cpu oracle: {cpu['value']} tok/s on {cpu['cores']} threads "
@@ -983,7 +1201,6 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_median_events": round(ev_step_ms, 4),
         "ms_per_step_min_events": round(min_step_ms, 4),
-        "ms_per_step_instrumented": round(inst_step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1005,14 +1222,19 @@ def main():
             "unit": "TFLOP/s", "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": traffic,
             "traffic_note": traffic_note,
             "kernel": ROOFLINE_KERNEL, "avg_launch_us": round(avg_launch_us, 2),
-            "launches_per_step": int(len(dom)),
+            "timing": "HIP events around graph replays of the 56 gate/up calls of a step "
+                      "(GEMM + tail reduce per call; host launch gaps excluded)",
+            "launches_per_step": 2 * layers,
             "algorithmic_bytes_per_call": M * 3584 * 2 + 18944 * 3584 * 2 + M * 18944 * 4,
         },
         "clock": clock,
         "dequant_roofline": {
             "bound": "hbm", "achieved": round(deq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(deq_gbs / PEAK_HBM_GBS, 4),
+            "hbm_copy_gbs": round(copy_gbs, 1),
+            "frac_of_copy": round(deq_gbs / copy_gbs, 4),
         },
+        "forward_check": fwd_check,
         "fused": fused,
         "mmq_forward": mmqf,
         "grouped_forward": grouped,

@@ -14,7 +14,8 @@
  *      spend 2 bytes per weight of extra device memory.
  *
  * Both feed the contraction the same f16 values (§3.3: the fused expansion
- * follows the standalone decode's rounding path bit for bit).
+ * follows the standalone decode's rounding path; the values are equal, only
+ * the sign of an exact zero may differ, which no f32 sum can see).
  *
  * Conventions shared by every entry point
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -185,9 +186,11 @@ int mq_gemm_f16cache(const uint16_t *X, int ldx, const uint16_t *W16, int ldw, f
  *   fmt : one of the MQ_Q* formats; K a multiple of its block.
  *   wq  : device, 16-byte aligned, N·mq_row_bytes(fmt, K) bytes.
  *   other arguments as mq_gemm_f16cache (ws sized with fmt).
- * The expanded f16 values are bit-identical to mq_dequant_to_f16's (minfer
- * 05 · 8p §3.3: same rounding path), so with the same X the two paths compute
- * the same product of the same operands. */
+ * The expanded f16 values equal mq_dequant_to_f16's in value (minfer 05 · 8p
+ * §3.3: same rounding path); only the sign of an exact zero may differ (the
+ * Q6_K, Q4_0 and Q5_0 expansions give +0 where the decode keeps −0).  A signed
+ * zero adds nothing to an f32 sum that starts at +0, so with the same X and
+ * the same K split the two paths return the same Y bit for bit. */
 int mq_gemm_fused(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y, int ldy,
                   int M, int N, int K, void *ws, size_t ws_bytes, int split_k, void *stream);
 
@@ -281,6 +284,36 @@ int64_t mq_gemm_mmq_workspace_bytes(int fmt, int M, int N, int K, int split_k);
 int mq_gemm_mmq(int fmt, const int8_t *Xq, int ldq, const float *ds, const void *wq, float *Y,
                 int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
                 void *stream);
+
+/* The launch plan of a GEMM call, as the host computes it (no GPU needed, no
+ * device call made).  For callers that size workspaces ahead and for tests
+ * of the planner.
+ *   path    : 0 = mq_gemm_f16cache (fmt 0) / mq_gemm_fused (fmt = format),
+ *             1 = their f32-activation variants, 2 = mq_gemm_mmq.
+ *   fmt, M, N, K, split_k : as the GEMM call would receive them.
+ *   out     : host struct, written on MQ_OK.
+ * The plan deals a BM × BN tile of Y to each workgroup: dp_tiles tiles over
+ * all of K, then tail_tiles tiles each split into `split` K ranges of
+ * steps_per_split k-steps (64 wide; 128 for path 2).  has_kernel is 1 when a
+ * kernel implements that tile for this format and 0 otherwise (the GEMM call
+ * would return MQ_ERR_HIP without launching).  ws_bytes equals what the
+ * matching *_workspace_bytes function returns.
+ * Errors: the argument checks of the GEMM call (MQ_ERR_FORMAT, MQ_ERR_SHAPE,
+ * MQ_ERR_SPLIT), MQ_ERR_NULL for out, MQ_ERR_FORMAT for an unknown path. */
+typedef struct mq_gemm_plan_info {
+    int bm, bn;              /* block tile: rows of X, rows of W */
+    int tiles_m, tiles_n;    /* ceil(M / bm), ceil(N / bn) */
+    int k_steps;             /* ceil(K / step) */
+    int dp_tiles;            /* tiles computed over all of K (the first ones) */
+    int tail_tiles;          /* tiles split along K */
+    int split;               /* K ranges per tail tile (1: no split) */
+    int steps_per_split;     /* k-steps per range */
+    int has_kernel;          /* 1: a kernel implements (bm, bn) for this format */
+    int64_t ws_bytes;        /* workspace the call needs */
+} mq_gemm_plan_info;
+
+int mq_gemm_plan_query(int path, int fmt, int M, int N, int K, int split_k,
+                       mq_gemm_plan_info *out);
 
 /* Static text for a return code (never NULL). */
 const char *mq_strerror(int code);

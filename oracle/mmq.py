@@ -2,11 +2,12 @@
 (see ``oracle/__init__``).
 
 Source: Fucina "Eager GPU Offload Without A Compute Graph", the section on
-what the ik_llama.cpp audit contributed: that MMQ quantizes each f32
-activation tile once to a Q8_1-style int8 layout (with scales and sums),
-unpacks the quantized weights into signed int8, multiplies with int8 matrix
-instructions, and so changes the activation numerics — a backend with its own
-parity gate, apart from the f16 contract.  minfer "05 · 8p" (§1, §6) and
+what the ik_llama.cpp audit contributed.  Read there: the int8 backend turns
+the f32 activations into int8 blocks carrying a scale and a code sum (the
+Q8_1 arrangement), turns the quantized weights into signed int8 codes, runs
+the contraction on the integer matrix units, and therefore computes with
+other activation values than the f16 paths — so it gets a parity gate of its
+own instead of the f16 tolerance.  minfer "05 · 8p" (§1, §6) and
 "79" (§1, §5) name the int8 MMQ prefill GEMM that streams raw quantized
 bytes.
 

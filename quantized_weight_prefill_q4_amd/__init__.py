@@ -29,6 +29,7 @@ from .api import (
     gemm_f16cache,
     gemm_fused,
     gemm_mmq,
+    gemm_plan,
     mmq_workspace_bytes,
     quantize_q8_1,
     row_bytes,
@@ -55,6 +56,7 @@ __all__ = [
     "gemm_f16cache",
     "gemm_fused",
     "gemm_mmq",
+    "gemm_plan",
     "lib",
     "mmq_workspace_bytes",
     "quantize_q8_1",

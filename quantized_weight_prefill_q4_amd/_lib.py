@@ -38,6 +38,14 @@ class MqDequantJob(ctypes.Structure):
                 ("wq", _vp), ("w16", _vp)]
 
 
+class MqGemmPlanInfo(ctypes.Structure):
+    """struct mq_gemm_plan_info of include/mq.h."""
+    _fields_ = [("bm", _c_int), ("bn", _c_int), ("tiles_m", _c_int), ("tiles_n", _c_int),
+                ("k_steps", _c_int), ("dp_tiles", _c_int), ("tail_tiles", _c_int),
+                ("split", _c_int), ("steps_per_split", _c_int), ("has_kernel", _c_int),
+                ("ws_bytes", _c_i64)]
+
+
 # name -> (restype, argtypes); mirrors include/mq.h
 SIGNATURES = {
     "mq_block_elems": (_c_int, [_c_int]),
@@ -61,6 +69,8 @@ SIGNATURES = {
     "mq_gemm_mmq_workspace_bytes": (_c_i64, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "mq_gemm_mmq": (_c_int, [_c_int, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                              _vp, _c_size, _c_int, _vp]),
+    "mq_gemm_plan_query": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    ctypes.POINTER(MqGemmPlanInfo)]),
     "mq_strerror": (ctypes.c_char_p, [_c_int]),
     "mq_last_hip_error": (_c_int, []),
 }

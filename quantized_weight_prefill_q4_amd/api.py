@@ -13,7 +13,7 @@ import torch
 import ctypes
 
 from ._lib import (MQ_Q4_0, MQ_Q4_K, MQ_Q5_0, MQ_Q5_1, MQ_Q5_K, MQ_Q6_K, MQ_Q8_0,
-                   MqDequantJob, check, lib)
+                   MqDequantJob, MqGemmPlanInfo, check, lib)
 
 FORMATS = {"q4_0": MQ_Q4_0, "q5_0": MQ_Q5_0, "q5_1": MQ_Q5_1, "q8_0": MQ_Q8_0,
            "q4_k": MQ_Q4_K, "q5_k": MQ_Q5_K, "q6_k": MQ_Q6_K}
@@ -88,6 +88,18 @@ def workspace_bytes(fmt, M: int, N: int, K: int, split_k: int = 0, x_f32: bool =
     f = 0 if fmt in (0, None, "f16") else _fmt(fmt)
     fn = "mq_gemm_xf32_workspace_bytes" if x_f32 else "mq_gemm_workspace_bytes"
     return check(getattr(lib(), fn)(f, M, N, K, split_k), fn)
+
+
+def gemm_plan(fmt, M: int, N: int, K: int, split_k: int = 0, path: str = "f16") -> dict:
+    """The launch plan of a GEMM call (host only): path "f16" for
+    gemm_f16cache / gemm_fused (fmt 0 / "f16" = the cache), "f32" for their
+    f32-activation variants, "mmq" for gemm_mmq."""
+    f = 0 if fmt in (0, None, "f16") else _fmt(fmt)
+    p = {"f16": 0, "f32": 1, "mmq": 2}[path]
+    info = MqGemmPlanInfo()
+    check(lib().mq_gemm_plan_query(p, f, M, N, K, split_k, ctypes.byref(info)),
+          "mq_gemm_plan_query")
+    return {name: getattr(info, name) for name, _ in MqGemmPlanInfo._fields_}
 
 
 def dequant_to_f16(wq: torch.Tensor, fmt, N: int, K: int, pad: bool = True,

@@ -100,8 +100,8 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
 
 hipError_t launch_gemm(int fmt, const uint16_t *X, int ldx, const void *W, int64_t ldw, float *Y,
                        int ldy, int M, int N, int K, const GemmPlan &plan, float *ws,
-                       hipStream_t stream) {
-    return launch_gemm_t<false>(fmt, X, ldx, W, ldw, Y, ldy, M, N, K, plan, ws, stream);
+                       hipStream_t stream, bool dry) {
+    return launch_gemm_t<false>(fmt, X, ldx, W, ldw, Y, ldy, M, N, K, plan, ws, stream, dry);
 }
 
 }  // namespace mq

@@ -229,6 +229,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
     int tm, tn;
     tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    // A tile at or past the matrix edge has nothing to compute; stopping
+    // here keeps every buffer range below built from a positive extent.
+    if (m0 >= a.M || n0 >= a.N) return;
     // K ranges are whole super-blocks (the plan's steps_per_split is a
     // multiple of 4, and K of 256)
     const int kt_begin = tail ? part * a.steps_per_split : 0;
@@ -473,6 +476,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
     int tm, tn;
     tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    // A tile at or past the matrix edge has nothing to compute; stopping
+    // here keeps every buffer range below built from a positive extent.
+    if (m0 >= a.M || n0 >= a.N) return;
     // K ranges start on even steps and (K a multiple of 256) end on even ones
     const int kt_begin = tail ? part * a.steps_per_split : 0;
     const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
@@ -780,6 +786,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
     int tm, tn;
     tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    // A tile at or past the matrix edge has nothing to compute; stopping
+    // here keeps every buffer range below built from a positive extent.
+    if (m0 >= a.M || n0 >= a.N) return;
     // K ranges start on even steps and (K a multiple of 256) end on even ones
     const int kt_begin = tail ? part * a.steps_per_split : 0;
     const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;

@@ -573,21 +573,21 @@ struct Q32Loader {
                 // d·q and 8d / 16d are exact in f32: one fma gives the
                 // decode's exact d·(q − 8) (only an exact zero's sign may
                 // differ, which the MFMA sums starting at +0 do not see)
-                const float c = -8.0f * d;
-                v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), c), __builtin_fmaf(d, ubyte_f32<1>(w0), c),
-                          __builtin_fmaf(d, ubyte_f32<2>(w0), c), __builtin_fmaf(d, ubyte_f32<3>(w0), c),
-                          __builtin_fmaf(d, ubyte_f32<0>(w1), c), __builtin_fmaf(d, ubyte_f32<1>(w1), c),
-                          __builtin_fmaf(d, ubyte_f32<2>(w1), c), __builtin_fmaf(d, ubyte_f32<3>(w1), c));
+                const float bias = -8.0f * d;
+                v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), bias), __builtin_fmaf(d, ubyte_f32<1>(w0), bias),
+                          __builtin_fmaf(d, ubyte_f32<2>(w0), bias), __builtin_fmaf(d, ubyte_f32<3>(w0), bias),
+                          __builtin_fmaf(d, ubyte_f32<0>(w1), bias), __builtin_fmaf(d, ubyte_f32<1>(w1), bias),
+                          __builtin_fmaf(d, ubyte_f32<2>(w1), bias), __builtin_fmaf(d, ubyte_f32<3>(w1), bias));
             } else {
                 const uint32_t hb = qh >> (8 * c);
                 w0 = opaque(w0 | spread4_to_bit4(hb & 15));
                 w1 = opaque(w1 | spread4_to_bit4((hb >> 4) & 15));
                 if constexpr (FMT == kFmtQ5_0) {
-                    const float c = -16.0f * d;
-                    v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), c), __builtin_fmaf(d, ubyte_f32<1>(w0), c),
-                              __builtin_fmaf(d, ubyte_f32<2>(w0), c), __builtin_fmaf(d, ubyte_f32<3>(w0), c),
-                              __builtin_fmaf(d, ubyte_f32<0>(w1), c), __builtin_fmaf(d, ubyte_f32<1>(w1), c),
-                              __builtin_fmaf(d, ubyte_f32<2>(w1), c), __builtin_fmaf(d, ubyte_f32<3>(w1), c));
+                    const float bias = -16.0f * d;
+                    v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), bias), __builtin_fmaf(d, ubyte_f32<1>(w0), bias),
+                              __builtin_fmaf(d, ubyte_f32<2>(w0), bias), __builtin_fmaf(d, ubyte_f32<3>(w0), bias),
+                              __builtin_fmaf(d, ubyte_f32<0>(w1), bias), __builtin_fmaf(d, ubyte_f32<1>(w1), bias),
+                              __builtin_fmaf(d, ubyte_f32<2>(w1), bias), __builtin_fmaf(d, ubyte_f32<3>(w1), bias));
                 } else {
                     const float m = f16_bits_to_f32(h0 >> 16);
                     v = pack8(__builtin_fmaf(d, ubyte_f32<0>(w0), m), __builtin_fmaf(d, ubyte_f32<1>(w0), m),
@@ -860,6 +860,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     int tm, tn;
     tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    // A tile at or past the matrix edge has nothing to compute; stopping
+    // here keeps every buffer range below built from a positive extent.
+    if (m0 >= a.M || n0 >= a.N) return;
     const int kt_begin = tail ? part * a.steps_per_split : 0;
     const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
 
@@ -992,7 +995,8 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ w
 }
 
 template <int BM, int BN, int FMT, bool XF32>
-hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
+hipError_t launch_tile(const Args &a, int grid, hipStream_t stream, bool dry) {
+    if (dry) return hipSuccess;
     // Tiles of 128 columns on 8 waves: two waves per SIMD double the LDS
     // throughput a step can draw on.  f16 cache: 1.5-4% faster at M = 128
     // and on the 7B q/o shape, no slower elsewhere.  Fused, with 128 or 256
@@ -1007,43 +1011,48 @@ hipError_t launch_tile(const Args &a, int grid, hipStream_t stream) {
 
 // The kernel for the plan's exact (BM, BN); a plan no kernel implements is an
 // error, never a launch with a mismatched tile (its grid would address tiles
-// past the matrix).
+// past the matrix).  dry: only report whether a kernel exists (hipSuccess)
+// or not (hipErrorInvalidValue), launching nothing.
 template <int FMT, bool XF32>
-hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t stream) {
+hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t stream, bool dry) {
     if (bm == 256 && bn == 256) {
         if constexpr ((FMT == kFmtQ4_K || FMT == kFmtQ5_K) && !XF32) {
+            if (dry) return hipSuccess;
             hipLaunchKernelGGL(gemm_q4k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
             return hipGetLastError();
         } else if constexpr (FMT == kFmtQ6_K && !XF32) {
+            if (dry) return hipSuccess;
             hipLaunchKernelGGL(gemm_q6k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
             return hipGetLastError();
         } else if constexpr ((FMT == kFmtQ8_0 || FMT == kFmtQ4_0 || FMT == kFmtQ5_0 ||
                               FMT == kFmtQ5_1) && !XF32) {
             if (a.K % 256 == 0) {   // rows of whole 8-block runs: 16-byte aligned
+                if (dry) return hipSuccess;
                 hipLaunchKernelGGL(gemm_b32_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream,
                                    a);
                 return hipGetLastError();
             }
-            return launch_tile<256, 256, FMT, XF32>(a, grid, stream);
+            return launch_tile<256, 256, FMT, XF32>(a, grid, stream, dry);
         } else if constexpr (!XF32) {
-            return launch_tile<256, 256, FMT, XF32>(a, grid, stream);
+            return launch_tile<256, 256, FMT, XF32>(a, grid, stream, dry);
         }
     } else if (bm == 256 && bn == 128) {
-        return launch_tile<256, 128, FMT, XF32>(a, grid, stream);
+        return launch_tile<256, 128, FMT, XF32>(a, grid, stream, dry);
     } else if (bm == 128 && bn == 128) {
-        return launch_tile<128, 128, FMT, XF32>(a, grid, stream);
+        return launch_tile<128, 128, FMT, XF32>(a, grid, stream, dry);
     } else if (bm == 64 && bn == 128) {
-        return launch_tile<64, 128, FMT, XF32>(a, grid, stream);
+        return launch_tile<64, 128, FMT, XF32>(a, grid, stream, dry);
     }
     return hipErrorInvalidValue;
 }
 
 // The plan's kernel for format `fmt` (kFmtF16: the f16 cache), then, for a
 // K split, the fixed-order reduction of the tail tiles' partial planes.
+// dry: check that the plan has a kernel and launch nothing.
 template <bool XF32>
 hipError_t launch_gemm_t(int fmt, const void *X, int ldx, const void *W, int64_t ldw, float *Y,
                          int ldy, int M, int N, int K, const GemmPlan &plan, float *ws,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool dry = false) {
     Args a;
     a.X = X;
     a.W = (const uint8_t *)W;
@@ -1064,17 +1073,17 @@ hipError_t launch_gemm_t(int fmt, const void *X, int ldx, const void *W, int64_t
     const int grid = plan.dp_tiles + plan.tail_tiles * plan.split;
     hipError_t e;
     switch (fmt) {
-    case kFmtQ4_K: e = launch_fmt<kFmtQ4_K, XF32>(a, plan.bm, plan.bn, grid, stream); break;
-    case kFmtQ6_K: e = launch_fmt<kFmtQ6_K, XF32>(a, plan.bm, plan.bn, grid, stream); break;
-    case kFmtQ8_0: e = launch_fmt<kFmtQ8_0, XF32>(a, plan.bm, plan.bn, grid, stream); break;
-    case kFmtQ4_0: e = launch_fmt<kFmtQ4_0, XF32>(a, plan.bm, plan.bn, grid, stream); break;
-    case kFmtQ5_0: e = launch_fmt<kFmtQ5_0, XF32>(a, plan.bm, plan.bn, grid, stream); break;
-    case kFmtQ5_1: e = launch_fmt<kFmtQ5_1, XF32>(a, plan.bm, plan.bn, grid, stream); break;
-    case kFmtQ5_K: e = launch_fmt<kFmtQ5_K, XF32>(a, plan.bm, plan.bn, grid, stream); break;
-    case kFmtF16: e = launch_fmt<kFmtF16, XF32>(a, plan.bm, plan.bn, grid, stream); break;
+    case kFmtQ4_K: e = launch_fmt<kFmtQ4_K, XF32>(a, plan.bm, plan.bn, grid, stream, dry); break;
+    case kFmtQ6_K: e = launch_fmt<kFmtQ6_K, XF32>(a, plan.bm, plan.bn, grid, stream, dry); break;
+    case kFmtQ8_0: e = launch_fmt<kFmtQ8_0, XF32>(a, plan.bm, plan.bn, grid, stream, dry); break;
+    case kFmtQ4_0: e = launch_fmt<kFmtQ4_0, XF32>(a, plan.bm, plan.bn, grid, stream, dry); break;
+    case kFmtQ5_0: e = launch_fmt<kFmtQ5_0, XF32>(a, plan.bm, plan.bn, grid, stream, dry); break;
+    case kFmtQ5_1: e = launch_fmt<kFmtQ5_1, XF32>(a, plan.bm, plan.bn, grid, stream, dry); break;
+    case kFmtQ5_K: e = launch_fmt<kFmtQ5_K, XF32>(a, plan.bm, plan.bn, grid, stream, dry); break;
+    case kFmtF16: e = launch_fmt<kFmtF16, XF32>(a, plan.bm, plan.bn, grid, stream, dry); break;
     default: e = hipErrorInvalidValue; break;
     }
-    if (e != hipSuccess || plan.split == 1) return e;
+    if (e != hipSuccess || plan.split == 1 || dry) return e;
     const int blocks = plan.tail_tiles * (plan.bm * plan.bn / 1024);
     hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, stream, ws, plan.split,
                        plan.tail_tiles, plan.dp_tiles, plan.bm, plan.bn, plan.tiles_m,

@@ -32,8 +32,8 @@ __global__ __launch_bounds__(256) void convert_f32_to_f16(const float *__restric
 
 hipError_t launch_gemm_xf32(int fmt, const float *X, int ldx, const void *W, int64_t ldw,
                             float *Y, int ldy, int M, int N, int K, const GemmPlan &plan,
-                            float *ws, hipStream_t stream) {
-    return launch_gemm_t<true>(fmt, X, ldx, W, ldw, Y, ldy, M, N, K, plan, ws, stream);
+                            float *ws, hipStream_t stream, bool dry) {
+    return launch_gemm_t<true>(fmt, X, ldx, W, ldw, Y, ldy, M, N, K, plan, ws, stream, dry);
 }
 
 hipError_t launch_convert_f32_to_f16(const float *X, int ldx, uint16_t *X16, int ld16, int M,

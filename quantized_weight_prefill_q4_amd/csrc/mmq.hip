@@ -501,6 +501,9 @@ __global__ __launch_bounds__(kThreads, 1) void mmq_kernel(MmqArgs a) {
     int tm, tn;
     tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    // A tile at or past the matrix edge has nothing to compute; stopping
+    // here keeps every buffer range below built from a positive extent.
+    if (m0 >= a.M || n0 >= a.N) return;
     const int kt_begin = tail ? part * a.steps_per_split : 0;
     const int kt_end = tail ? min(kt_begin + a.steps_per_split, a.k_steps) : a.k_steps;
     const int nblk = a.K >> 5;
@@ -669,6 +672,8 @@ hipError_t launch_quantize_q8_1(const float *X, int ldx, int8_t *Xq, int ldq, fl
                        Xq, ldq, ds, K / 32, chunks, cpr);
     return hipGetLastError();
 }
+
+bool mmq_plan_has_kernel(const GemmPlan &p) { return p.bm == kMmqBM && p.bn == kMmqBN; }
 
 // The f16 GEMM's rule with 128 × 128 tiles and 128-wide k-steps: whole rounds
 // of kCUs tiles over all of K, the last partial round split along K (at

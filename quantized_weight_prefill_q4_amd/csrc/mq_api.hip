@@ -284,6 +284,51 @@ int mq_gemm_mmq(int fmt, const int8_t *Xq, int ldq, const float *ds, const void 
                                      (float *)ws, (hipStream_t)stream));
 }
 
+int mq_gemm_plan_query(int path, int fmt, int M, int N, int K, int split_k,
+                       mq_gemm_plan_info *out) {
+    if (!out) return MQ_ERR_NULL;
+    if (path < 0 || path > 2) return MQ_ERR_FORMAT;
+    const bool mmq = path == 2;
+    if (mmq ? !quant_fmt(fmt) : (fmt != mq::kFmtF16 && !quant_fmt(fmt))) return MQ_ERR_FORMAT;
+    if (int rc = check_dims(M, N, K)) return rc;
+    if (K % (fmt == mq::kFmtF16 ? 8 : mq::block_elems(fmt)) || (mmq && K % 32))
+        return MQ_ERR_SHAPE;
+    if (split_k < 0 || split_k > MQ_MAX_SPLIT_K) return MQ_ERR_SPLIT;
+    if (split_k > 1 && (int64_t)M * N >= ((int64_t)1 << 31)) return MQ_ERR_SPLIT;
+    mq::GemmPlan p;
+    int64_t x16_bytes = 0;
+    bool has_kernel;
+    if (mmq) {
+        p = mq::plan_mmq(M, N, K, split_k);
+        has_kernel = mq::mmq_plan_has_kernel(p);
+    } else if (path == 1) {
+        const XPlan xp = xf32_plan(fmt, M, N, K, split_k);
+        p = xp.gemm;
+        x16_bytes = xp.x16_bytes;
+        has_kernel = (xp.convert_first
+                          ? mq::launch_gemm(fmt, nullptr, 0, nullptr, 0, nullptr, 0, M, N, K, p,
+                                            nullptr, nullptr, true)
+                          : mq::launch_gemm_xf32(fmt, nullptr, 0, nullptr, 0, nullptr, 0, M, N,
+                                                 K, p, nullptr, nullptr, true)) == hipSuccess;
+    } else {
+        p = mq::plan_gemm(fmt, M, N, K, split_k);
+        has_kernel = mq::launch_gemm(fmt, nullptr, 0, nullptr, 0, nullptr, 0, M, N, K, p,
+                                     nullptr, nullptr, true) == hipSuccess;
+    }
+    out->bm = p.bm;
+    out->bn = p.bn;
+    out->tiles_m = p.tiles_m;
+    out->tiles_n = p.tiles_n;
+    out->k_steps = p.k_steps;
+    out->dp_tiles = p.dp_tiles;
+    out->tail_tiles = p.tail_tiles;
+    out->split = p.split;
+    out->steps_per_split = p.steps_per_split;
+    out->has_kernel = has_kernel ? 1 : 0;
+    out->ws_bytes = x16_bytes + p.ws_bytes;
+    return MQ_OK;
+}
+
 const char *mq_strerror(int code) {
     switch (code) {
     case MQ_OK: return "success";

@@ -70,21 +70,23 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32 = fal
 // Launch the GEMM (and the split-K reduction when plan.split > 1).
 //   W    : uint16 f16 cache when fmt == kFmtF16, else quantized bytes.
 //   ldw  : f16 row stride (elements) or quantized row bytes.
+//   dry  : launch nothing; hipSuccess iff a kernel implements the plan.
 hipError_t launch_gemm(int fmt, const uint16_t *X, int ldx, const void *W, int64_t ldw,
                        float *Y, int ldy, int M, int N, int K, const GemmPlan &plan, float *ws,
-                       hipStream_t stream);
+                       hipStream_t stream, bool dry = false);
 
 // The same GEMM with f32 activations X (row stride ldx in elements), each
 // rounded to f16 as its tile is staged; plan from plan_gemm(..., true).
 hipError_t launch_gemm_xf32(int fmt, const float *X, int ldx, const void *W, int64_t ldw,
                             float *Y, int ldy, int M, int N, int K, const GemmPlan &plan,
-                            float *ws, hipStream_t stream);
+                            float *ws, hipStream_t stream, bool dry = false);
 
 // The int8 product: Q8_1-style activation blocks (codes Xq, row stride ldq;
 // (d, s) pairs ds, [M][K/32]) and the plan and launch of the MMQ kernel.
 hipError_t launch_quantize_q8_1(const float *X, int ldx, int8_t *Xq, int ldq, float *ds, int M,
                                 int K, hipStream_t stream);
 GemmPlan plan_mmq(int M, int N, int K, int split_req);
+bool mmq_plan_has_kernel(const GemmPlan &p);   // the int8 kernel's tile is the plan's
 hipError_t launch_mmq(int fmt, const int8_t *Xq, int ldq, const float *ds, const void *W,
                       int64_t ldw, float *Y, int ldy, int M, int N, int K, const GemmPlan &plan,
                       float *ws, hipStream_t stream);
