@@ -644,7 +644,7 @@ def forward_sample(torch, W, xa, xf, ys, M):
     and the quantized bytes and f16-cache rows of the FWD_COLS weight rows.
     Rows and columns are seeded draws that include the first and the last."""
     g = np.random.default_rng(7004)
-    rows = np.unique(np.concatenate([[0, M - 1], g.choice(M, FWD_ROWS - 2, replace=False)]))
+    rows = np.sort(np.concatenate([[0, M - 1], 1 + g.choice(M - 2, FWD_ROWS - 2, replace=False)]))
     torch.cuda.synchronize()
     ridx = torch.from_numpy(rows).to(xa.device)
 
@@ -653,7 +653,7 @@ def forward_sample(torch, W, xa, xf, ys, M):
 
     out = {"rows": rows, "x": {"a": bits(xa[ridx]), "f": bits(xf[ridx])}, "mats": {}}
     for name, (fmt, N, K, q, cache) in W[-1].items():
-        cols = np.unique(np.concatenate([[0, N - 1], g.choice(N, FWD_COLS - 2, replace=False)]))
+        cols = np.sort(np.concatenate([[0, N - 1], 1 + g.choice(N - 2, FWD_COLS - 2, replace=False)]))
         cidx = torch.from_numpy(cols).to(xa.device)
         rb = q.numel() // N
         out["mats"][name] = {
