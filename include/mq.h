@@ -88,13 +88,17 @@ enum {
     MQ_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
     MQ_ERR_WORKSPACE = -6, /* workspace missing or smaller than mq_gemm_workspace_bytes */
     MQ_ERR_SPLIT = -7,     /* split_k outside 0..MQ_MAX_SPLIT_K */
-    MQ_ERR_HIP = -8        /* the HIP runtime rejected a launch; see mq_last_hip_error */
+    MQ_ERR_HIP = -8,       /* the HIP runtime rejected a launch; see mq_last_hip_error */
+    MQ_ERR_SCRATCH = -9    /* mq_gemm_fused_noalloc: the plan's partial tiles exceed
+                              MQ_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Limits checked by every entry point. */
 #define MQ_MAX_DIM (1 << 24)     /* M and N */
 #define MQ_MAX_K (1 << 21)       /* K and every leading dimension */
 #define MQ_MAX_SPLIT_K 16
+/* Static device scratch of mq_gemm_fused_noalloc, per GPU (64 MiB). */
+#define MQ_NOALLOC_SCRATCH_BYTES (64 << 20)
 
 /* Elements per block of `fmt` (32 or 256), or MQ_ERR_FORMAT. */
 int mq_block_elems(int fmt);
@@ -193,6 +197,29 @@ int mq_gemm_f16cache(const uint16_t *X, int ldx, const uint16_t *W16, int ldw, f
  * the same K split the two paths return the same Y bit for bit. */
 int mq_gemm_fused(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y, int ldy,
                   int M, int N, int K, void *ws, size_t ws_bytes, int split_k, void *stream);
+
+/* mq_gemm_fused for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, plan, kernels and result as mq_gemm_fused (bit for bit),
+ * but the K-split partial tiles go to a static array of the library instead
+ * of a caller workspace; nothing is allocated or freed (not by the library,
+ * not through torch).
+ *   split_k : as mq_gemm_fused.  The automatic plan always fits the scratch
+ *             (it splits at most kCUs = 256 tiles of at most 256 × 256 f32, i.e.
+ *             exactly MQ_NOALLOC_SCRATCH_BYTES); a forced split whose partial
+ *             tiles, mq_gemm_workspace_bytes(fmt, M, N, K, split_k), exceed
+ *             MQ_NOALLOC_SCRATCH_BYTES returns MQ_ERR_SCRATCH and runs nothing.
+ *   stream  : the scratch used is the one of the device that owns `stream`
+ *             (the current device for NULL).  Its address is looked up once
+ *             per device, on the first call there, with hipGetSymbolAddress.
+ * Each GPU has ONE scratch: calls that may overlap on the same GPU (other
+ * streams, other host threads) race on it and must be ordered by the caller.
+ * Every partial tile is written in full before it is read, so nothing in it
+ * has to start at zero; it keeps the last call's partials.
+ * Errors: as mq_gemm_fused, plus MQ_ERR_SCRATCH (and MQ_ERR_HIP if the
+ * symbol lookup fails). */
+int mq_gemm_fused_noalloc(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y,
+                          int ldy, int M, int N, int K, int split_k, void *stream);
 
 /* f32 activations.  Fucina "Eager GPU Offload Without A Compute Graph",
  * quantized linears: the callers hold f32 activations, and the GEMM rounds

@@ -19,6 +19,8 @@ MQ_ERR_ALIGN = -5
 MQ_ERR_WORKSPACE = -6
 MQ_ERR_SPLIT = -7
 MQ_ERR_HIP = -8
+MQ_ERR_SCRATCH = -9
+MQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MQ_Q4_0 = 2
 MQ_Q5_0 = 6
@@ -59,6 +61,8 @@ SIGNATURES = {
                                   _vp, _c_size, _c_int, _vp]),
     "mq_gemm_fused": (_c_int, [_c_int, _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                _vp, _c_size, _c_int, _vp]),
+    "mq_gemm_fused_noalloc": (_c_int, [_c_int, _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                                       _c_int, _c_int, _vp]),
     "mq_gemm_xf32_workspace_bytes": (_c_i64, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "mq_gemm_f16cache_xf32": (_c_int, [_vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
                                        _c_int, _vp, _c_size, _c_int, _vp]),

@@ -7,7 +7,15 @@
 #include "mq.h"
 #include "mq_internal.h"
 
+#include <mutex>
 #include <stdint.h>
+
+// The K-split partial tiles of mq_gemm_fused_noalloc, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy for the life of
+// the process.  In host code `scratch` names a host-side stand-in: kernels get
+// the device address that hipGetSymbolAddress returns for the device
+// (scratch_ptr below), never the array's name.
+static __device__ __align__(256) float scratch[MQ_NOALLOC_SCRATCH_BYTES / 4];
 
 namespace {
 
@@ -77,6 +85,40 @@ XPlan xf32_plan(int fmt, int M, int N, int K, int split_k) {
         xp.gemm = mq::plan_gemm(fmt, M, N, K, split_k, true);
     }
     return xp;
+}
+
+// Device address of `scratch` on the device that owns `stream` (the current
+// device for the null stream), looked up once per device with that device
+// current and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_ptr(hipStream_t stream, void **out) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    dev = cur;
+    if (stream) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return hip_status(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MQ_OK;
 }
 
 // Shared checks of both GEMM entry points; fills the plan on success.
@@ -214,6 +256,26 @@ int mq_gemm_fused(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y,
                                       (float *)ws, (hipStream_t)stream));
 }
 
+int mq_gemm_fused_noalloc(int fmt, const uint16_t *X, int ldx, const void *wq, float *Y,
+                          int ldy, int M, int N, int K, int split_k, void *stream) {
+    if (!quant_fmt(fmt)) return MQ_ERR_FORMAT;
+    // the plan's partial tiles must fit the static scratch
+    const int64_t need = mq_gemm_workspace_bytes(fmt, M, N, K, split_k);
+    if (need < 0) return (int)need;
+    if (need > MQ_NOALLOC_SCRATCH_BYTES) return MQ_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        if (int rc = scratch_ptr((hipStream_t)stream, &ws)) return rc;
+    }
+    mq::GemmPlan plan;
+    if (int rc = check_gemm(fmt, X, ldx, wq, 0, Y, ldy, M, N, K, ws,
+                            need > 0 ? (size_t)MQ_NOALLOC_SCRATCH_BYTES : 0, split_k, &plan))
+        return rc;
+    const int64_t row_bytes = (int64_t)K / mq::block_elems(fmt) * mq::block_bytes(fmt);
+    return hip_status(mq::launch_gemm(fmt, X, ldx, wq, row_bytes, Y, ldy, M, N, K, plan,
+                                      (float *)ws, (hipStream_t)stream));
+}
+
 int mq_gemm_f16cache_xf32(const float *X, int ldx, const uint16_t *W16, int ldw, float *Y,
                           int ldy, int M, int N, int K, void *ws, size_t ws_bytes, int split_k,
                           void *stream) {
@@ -340,6 +402,7 @@ const char *mq_strerror(int code) {
     case MQ_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than required";
     case MQ_ERR_SPLIT: return "split_k out of range for this problem";
     case MQ_ERR_HIP: return "the HIP runtime rejected a launch";
+    case MQ_ERR_SCRATCH: return "the K-split partial tiles exceed the static scratch (MQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
     }
 }
