@@ -36,6 +36,12 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
         // us; 18944 × 3584 at M = 768 -13%; fused -10%).
         if (t256 >= kCUs || split_fills || t256 * 4 > kCUs * 3) p.bn = 256;
     }
+    // (Fused formats at M <= 128 keep the 2 × 2 tiles: the register-expansion
+    // kernels on 128 × 256 tiles, with about 2.6 times less LDS traffic per
+    // flop, measured slower on every M = 128 sweep shape — 4096 × 4096
+    // 22.2 -> 26.5 us, 4096 × 14336 34.8 -> 37.6 us — so LDS is not what
+    // bounds a small-M step.)
+    const bool b32 = fmt == kFmtQ8_0 || fmt == kFmtQ4_0 || fmt == kFmtQ5_0 || fmt == kFmtQ5_1;
     // Narrow outputs (the 256 × 128 grid has at most kCUs / 4 tiles, e.g. the
     // 7B k/v projections, N = 512) with a short K take 64-row tiles: four
     // times the tiles, so a two-way K split instead of eight fills the
@@ -80,13 +86,12 @@ GemmPlan plan_gemm(int fmt, int M, int N, int K, int split_req, bool x_f32) {
     if (split > k64) split = k64;
     int per = (k64 + split - 1) / split;
     // the fused Q6_K loader pairs k-steps (2j, 2j + 1), and so does the fused
-    // 256 × 256 kernel of the 32-element block formats (K a multiple of 256):
-    // ranges start even; the fused Q4_K 256 × 256 kernel stages whole
-    // super-blocks (4 steps), and so does the fused Q5_K one
-    const bool b32 = fmt == kFmtQ8_0 || fmt == kFmtQ4_0 || fmt == kFmtQ5_0 || fmt == kFmtQ5_1;
-    const bool pairs = fmt == kFmtQ6_K || (b32 && p.bm == 256 && p.bn == 256 && K % 256 == 0);
+    // register-expansion kernel of the 32-element block formats (256-column
+    // tiles, K a multiple of 256): ranges start even; the fused Q4_K and
+    // Q5_K register-expansion kernels stage whole super-blocks (4 steps)
+    const bool pairs = fmt == kFmtQ6_K || (b32 && p.bn == 256 && K % 256 == 0);
     if (pairs && (per & 1) && split > 1) ++per;
-    if ((fmt == kFmtQ4_K || fmt == kFmtQ5_K) && p.bm == 256 && p.bn == 256 && split > 1)
+    if ((fmt == kFmtQ4_K || fmt == kFmtQ5_K) && p.bn == 256 && split > 1)
         per = (per + 3) / 4 * 4;
     split = (k64 + per - 1) / per;   // no empty range
     if (split == 1) dp = tiles;

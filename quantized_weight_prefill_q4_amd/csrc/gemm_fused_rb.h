@@ -162,17 +162,17 @@ __device__ __forceinline__ void rb_fetch(const u32x4 *Bc, int lane, int wave, Rb
 // One k-step of the wave's 256 × 64 tile from X stage Ac and the raw bytes
 // `cur` (fetched during the previous step); fetches the next step's raw
 // bytes (quarter NC4 of buffer Bnext) into `nxt` between the MFMAs.
-template <int FMT, int NC4, class Slot>
-__device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32x16 (&acc)[8][2],
+template <int FMT, int NC4, int FM, class Slot>
+__device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32x16 (&acc)[FM][2],
                                         int lane, int wave, const RbRaw &cur, RbRaw &nxt,
                                         Slot &&slot) {
     const int h = lane >> 5;
-    half8 af[2][8], bf[2][2];
-    auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
+    half8 af[2][FM], bf[2][2];
+    auto load_a = [&](auto KKc, half8(&dst)[FM]) MQ_INLINE {
         constexpr int kk = KKc;
         const int c = kk * 2 + h;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < FM; ++i) {
             const int r = i * 32 + (lane & 31);
             dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
         }
@@ -190,8 +190,8 @@ __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32
             rb_fetch<FMT, NC4>(Bnext, lane, wave, nxt);
         }
         __builtin_amdgcn_sched_barrier(0);
-        static_for<16>([&](auto IJ) MQ_INLINE {
-            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 16 + IJ;
+        static_for<2 * FM>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
             acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
                                                                0);
             if constexpr (n & 1) {
@@ -203,12 +203,13 @@ __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32
     });
 }
 
-template <int FMT>
+template <int FMT, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
     static_assert(FMT == kFmtQ4_K || FMT == kFmtQ5_K, "Q4_K or Q5_K");
     using G = KRb<FMT>;
-    constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
-    constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
+    static_assert(BM == 64 || BM == 128 || BM == 256, "tiles of 64, 128 or 256 rows");
+    constexpr int BN = 256, BK = 64, CPR = 8;
+    constexpr int FM = BM / 32, FN = 2, TM = BM, TN = 64;
     constexpr int NT = G::CH;   // chunks per thread (256 rows × CH over 256 threads)
     __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
     __shared__ u32x4 Bq0[256 * G::CH], Bq1[256 * G::CH];
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
         constexpr int LC = (C4 + 1) & 3;
         constexpr int NL = RbPart<FMT, LC>::hi - RbPart<FMT, LC>::lo;
         constexpr int NS = RbPart<FMT, C4>::hi - RbPart<FMT, C4>::lo;
-        constexpr int H = 16;
+        constexpr int H = 2 * FM;   // half the step's slots
         u32x4 *An = P ? A0 : A1;
         const int sb = kt >> 2;
         const u32x4 *Bc = (sb & 1) ? Bq1 : Bq0;
@@ -337,7 +338,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
         step(std::integral_constant<int, 3>(), kt + 3);
     }
 
-    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+    // the 16-byte-store epilogue's patches: the X stages when they are large
+    // enough (256 rows), else the raw-weight buffers (idle after the loop too)
+    if constexpr (BM == 256)
+        store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+    else
+        store_tile<BM, BN, FM, FN, TM, TN, (int)sizeof(Bq0)>(a, acc, tail, part, tile, m0, n0, wm,
+                                                             wn, lane, wave, Bq0, Bq1);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,18 +419,18 @@ __device__ __forceinline__ half8 q6k_frag(const R6Raw &r, int f) {
     return __builtin_bit_cast(half8, q6k_chunk(q0, q1, r.ds[f][KK]));
 }
 
-template <int C2, class Slot>
+template <int C2, int FM, class Slot>
 __device__ __forceinline__ void rb6_step(const u32x4 *Ac, const u32x4 *Bc, int h,
-                                         f32x16 (&acc)[8][2], int lane, int wave, Slot &&slot) {
+                                         f32x16 (&acc)[FM][2], int lane, int wave, Slot &&slot) {
     const int hl = lane >> 5;
     R6Raw raw;
     r6_fetch<C2>(Bc, h, lane, wave, raw);
-    half8 af[2][8], bf[2][2];
-    auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
+    half8 af[2][FM], bf[2][2];
+    auto load_a = [&](auto KKc, half8(&dst)[FM]) MQ_INLINE {
         constexpr int kk = KKc;
         const int c = kk * 2 + hl;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < FM; ++i) {
             const int r = i * 32 + (lane & 31);
             dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
         }
@@ -439,8 +446,8 @@ __device__ __forceinline__ void rb6_step(const u32x4 *Ac, const u32x4 *Bc, int h
             bf[c ^ 1][1] = q6k_frag<C2, kk + 1>(raw, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        static_for<16>([&](auto IJ) MQ_INLINE {
-            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 16 + IJ;
+        static_for<2 * FM>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
             acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
                                                                0);
             if constexpr (n & 1) {
@@ -452,11 +459,12 @@ __device__ __forceinline__ void rb6_step(const u32x4 *Ac, const u32x4 *Bc, int h
     });
 }
 
-template <int FMT>
+template <int FMT, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
     static_assert(FMT == kFmtQ6_K, "Q6_K only");
-    constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
-    constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
+    static_assert(BM == 64 || BM == 128 || BM == 256, "tiles of 64, 128 or 256 rows");
+    constexpr int BN = 256, BK = 64, CPR = 8;
+    constexpr int FM = BM / 32, FN = 2, TM = BM, TN = 64;
     __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
     __shared__ u32x4 Bq0[256 * kR6Stride], Bq1[256 * kR6Stride];
 
@@ -550,7 +558,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
     // into set P; slots 16..31 write set 1 − P (part C2 of half kt/2 + 1).
     auto step = [&](auto C2c, int kt) MQ_INLINE {
         constexpr int C2 = decltype(C2c)::value, P = C2;
-        constexpr int H = 16, NB = 4;
+        constexpr int H = 2 * FM, NB = 4;   // H: half the step's slots
         u32x4 *An = P ? A0 : A1;
         const int hx = kt >> 1;
         const u32x4 *Bc = (hx & 1) ? Bq1 : Bq0;
@@ -579,7 +587,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
         step(std::integral_constant<int, 0>(), kt);
         step(std::integral_constant<int, 1>(), kt + 1);
     }
-    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+    // the 16-byte-store epilogue's patches: the X stages when they are large
+    // enough (256 rows), else the raw-weight buffers (idle after the loop too)
+    if constexpr (BM == 256)
+        store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+    else
+        store_tile<BM, BN, FM, FN, TM, TN, (int)sizeof(Bq0)>(a, acc, tail, part, tile, m0, n0, wm,
+                                                             wn, lane, wave, Bq0, Bq1);
 }
 
 
@@ -720,18 +734,18 @@ __device__ __forceinline__ half8 b32_frag(const B32Raw &r, int f) {
     }
 }
 
-template <int FMT, int C2, class Slot>
+template <int FMT, int C2, int FM, class Slot>
 __device__ __forceinline__ void b32_step(const u32x4 *Ac, const u32x4 *Bc, int o4,
-                                         f32x16 (&acc)[8][2], int lane, int wave, Slot &&slot) {
+                                         f32x16 (&acc)[FM][2], int lane, int wave, Slot &&slot) {
     const int hl = lane >> 5;
     B32Raw raw;
     b32_fetch<FMT, C2>(Bc, o4, lane, wave, raw);
-    half8 af[2][8], bf[2][2];
-    auto load_a = [&](auto KKc, half8(&dst)[8]) MQ_INLINE {
+    half8 af[2][FM], bf[2][2];
+    auto load_a = [&](auto KKc, half8(&dst)[FM]) MQ_INLINE {
         constexpr int kk = KKc;
         const int c = kk * 2 + hl;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < FM; ++i) {
             const int r = i * 32 + (lane & 31);
             dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
         }
@@ -747,8 +761,8 @@ __device__ __forceinline__ void b32_step(const u32x4 *Ac, const u32x4 *Bc, int o
             bf[c ^ 1][1] = b32_frag<FMT, kk + 1>(raw, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        static_for<16>([&](auto IJ) MQ_INLINE {
-            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 16 + IJ;
+        static_for<2 * FM>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
             acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
                                                                0);
             if constexpr (n & 1) {
@@ -760,11 +774,12 @@ __device__ __forceinline__ void b32_step(const u32x4 *Ac, const u32x4 *Bc, int o
     });
 }
 
-template <int FMT>
+template <int FMT, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
     using G = B32Rb<FMT>;
-    constexpr int BM = 256, BN = 256, BK = 64, CPR = 8;
-    constexpr int FM = 8, FN = 2, TM = 256, TN = 64;
+    static_assert(BM == 64 || BM == 128 || BM == 256, "tiles of 64, 128 or 256 rows");
+    constexpr int BN = 256, BK = 64, CPR = 8;
+    constexpr int FM = BM / 32, FN = 2, TM = BM, TN = 64;
     constexpr int HB = 4 * G::BB;                  // bytes of a half run
     constexpr int OODD = (HB % 16) / 4;            // odd halves: first block at this dword
     __shared__ u32x4 A0[BM * CPR], A1[BM * CPR];
@@ -858,7 +873,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
     // into set P; slots 16..31 write set 1 − P (part C2 of half kt/2 + 1).
     auto step = [&](auto C2c, int kt) MQ_INLINE {
         constexpr int C2 = decltype(C2c)::value, P = C2;
-        constexpr int H = 16;
+        constexpr int H = 2 * FM;   // half the step's slots
         constexpr int lpart = 1 - C2;
         constexpr int NBL = B32Part<FMT, lpart>::hi - B32Part<FMT, lpart>::lo;
         constexpr int NBS = B32Part<FMT, C2>::hi - B32Part<FMT, C2>::lo;
@@ -889,7 +904,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
         step(std::integral_constant<int, 0>(), kt);
         step(std::integral_constant<int, 1>(), kt + 1);
     }
-    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+    // the 16-byte-store epilogue's patches: the X stages when they are large
+    // enough (256 rows), else the raw-weight buffers (idle after the loop too)
+    if constexpr (BM == 256)
+        store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+    else
+        store_tile<BM, BN, FM, FN, TM, TN, (int)sizeof(Bq0)>(a, acc, tail, part, tile, m0, n0, wm,
+                                                             wn, lane, wave, Bq0, Bq1);
 }
 
 }  // namespace

@@ -742,9 +742,10 @@ __device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x1
 // partial tile to slot (part, tail tile) of the workspace.  C layout of a
 // 32x32 MFMA block: the lane holds column (lane & 31) and rows
 // 8·(r/4) + 4·(lane/32) + r%4 for accumulator element r; rows and columns of
-// a partial tile past M/N hold zeros.  S0, S1: the workgroup's two X stages,
-// idle once the k-loop is done.
-template <int BM, int BN, int FM, int FN, int TM, int TN>
+// a partial tile past M/N hold zeros.  S0, S1: two LDS buffers of PATCH
+// bytes each, idle once the k-loop is done (by default the workgroup's two X
+// stages).
+template <int BM, int BN, int FM, int FN, int TM, int TN, int PATCH = BM * 8 * 16>
 __device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN], bool tail,
                                            int part, int tile, int m0, int n0, int wm, int wn,
                                            int lane, int wave, u32x4 *S0, u32x4 *S1) {
@@ -763,15 +764,14 @@ __device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN],
         cols = a.N - n0;
     }
     const int col_l = lane & 31, row_l = (lane >> 5) * 4;
-    if constexpr (BM == 256) {
+    constexpr int PS = 36;   // patch row stride in floats (keeps 16-byte rows)
+    if constexpr (BM >= 64 && 4 * 32 * PS * 4 <= PATCH) {
         // Full tile, 16-byte-aligned rows: each 32x32 block goes through a
-        // private 32 x 36-float LDS patch of the wave (waves 0-3 in the first
-        // A stage, 4-7 in the second, both idle after the last step) so that
-        // every lane then stores 4 consecutive columns of one row — a quarter
-        // of the store instructions of the column-per-lane layout.
+        // private 32 x 36-float LDS patch of the wave (waves 0-3 in S0, 4-7
+        // in S1, both idle after the last step) so that every lane then
+        // stores 4 consecutive columns of one row — a quarter of the store
+        // instructions of the column-per-lane layout.
         if (rows >= BM && cols >= BN && (ldo & 3) == 0) {
-            constexpr int PS = 36;   // patch row stride in floats (keeps 16-byte rows)
-            static_assert(4 * 32 * PS * 4 <= BM * 8 * 16, "patches exceed an X stage");
             float *patch = reinterpret_cast<float *>(wave < 4 ? S0 : S1) + (wave & 3) * (32 * PS);
             sync_lds();              // every wave is done reading the stages
             const int rr = lane >> 3, cc = 4 * (lane & 7);
@@ -967,10 +967,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
 namespace mq {
 namespace {
 
-// Y tile = Σ_s partial[s] in the order s = 0, 1, ..., split − 1, for every
-// tail tile.  Block (tail tile, chunk) handles 1024 consecutive elements of
-// the BM × BN partial tile, four per thread.
-__global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ ws, int split,
+// Y tile = Σ_s partial[s] in the order s = 0, 1, ..., S − 1, for every tail
+// tile.  Block (tail tile, chunk) handles 1024 consecutive elements of the
+// BM × BN partial tile, four per thread.  All S loads of a thread are issued
+// before the first add (S is a compile-time constant), so the partials
+// stream in parallel instead of one memory latency per partial.
+template <int S>
+__global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ ws,
                                                      int tail_tiles, int dp_tiles, int bm, int bn,
                                                      int tiles_m, int tiles_n,
                                                      float *__restrict__ Y, int ldy, int M, int N) {
@@ -984,14 +987,38 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ w
     if (row >= M || col >= N) return;
     const int64_t tile_elems = (int64_t)bm * bn, stride = tile_elems * tail_tiles;
     const float *p = ws + tt * tile_elems + e;
-    f32x4 acc = *(const f32x4 *)p;
-    for (int s = 1; s < split; ++s) acc += *(const f32x4 *)(p + s * stride);
+    f32x4 v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) v[s] = *(const f32x4 *)(p + s * stride);
+    f32x4 acc = v[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) acc += v[s];
     float *y = Y + (int64_t)row * ldy + col;
     const int n = min(4, N - col);
+    if (n == 4 && (ldy & 3) == 0) {   // Y is 16-byte aligned, and so is this row piece
+        *(f32x4 *)y = acc;
+        return;
+    }
     y[0] = acc.x;
     if (n > 1) y[1] = acc.y;
     if (n > 2) y[2] = acc.z;
     if (n > 3) y[3] = acc.w;
+}
+
+// The reduce of `split` partial planes (2 .. 16).
+template <int S = 2>
+hipError_t launch_splitk_reduce(int split, dim3 grid, hipStream_t stream, const float *ws,
+                                int tail_tiles, int dp_tiles, int bm, int bn, int tiles_m,
+                                int tiles_n, float *Y, int ldy, int M, int N) {
+    if constexpr (S <= 16) {
+        if (split != S)
+            return launch_splitk_reduce<S + 1>(split, grid, stream, ws, tail_tiles, dp_tiles, bm,
+                                               bn, tiles_m, tiles_n, Y, ldy, M, N);
+        hipLaunchKernelGGL(splitk_reduce<S>, grid, dim3(256), 0, stream, ws, tail_tiles,
+                           dp_tiles, bm, bn, tiles_m, tiles_n, Y, ldy, M, N);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, int FMT, bool XF32>
@@ -1009,6 +1036,29 @@ hipError_t launch_tile(const Args &a, int grid, hipStream_t stream, bool dry) {
     return hipGetLastError();
 }
 
+// The register-expansion fused kernel of format FMT on BM × 256 tiles
+// (Q4_K and Q5_K, Q6_K, and the 32-element block formats when K is a
+// multiple of 256); hipErrorNotSupported when there is none.
+template <int FMT, int BM>
+hipError_t launch_rb(const Args &a, int grid, hipStream_t stream, bool dry) {
+    if constexpr (FMT == kFmtQ4_K || FMT == kFmtQ5_K) {
+        if (dry) return hipSuccess;
+        hipLaunchKernelGGL((gemm_q4k_rb_kernel<FMT, BM>), dim3(grid), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    } else if constexpr (FMT == kFmtQ6_K) {
+        if (dry) return hipSuccess;
+        hipLaunchKernelGGL((gemm_q6k_rb_kernel<FMT, BM>), dim3(grid), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    } else if constexpr (FMT == kFmtQ8_0 || FMT == kFmtQ4_0 || FMT == kFmtQ5_0 ||
+                         FMT == kFmtQ5_1) {
+        if (a.K % 256 != 0) return hipErrorNotSupported;   // rows of whole 8-block runs only
+        if (dry) return hipSuccess;
+        hipLaunchKernelGGL((gemm_b32_rb_kernel<FMT, BM>), dim3(grid), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
+    return hipErrorNotSupported;
+}
+
 // The kernel for the plan's exact (BM, BN); a plan no kernel implements is an
 // error, never a launch with a mismatched tile (its grid would address tiles
 // past the matrix).  dry: only report whether a kernel exists (hipSuccess)
@@ -1016,26 +1066,11 @@ hipError_t launch_tile(const Args &a, int grid, hipStream_t stream, bool dry) {
 template <int FMT, bool XF32>
 hipError_t launch_fmt(const Args &a, int bm, int bn, int grid, hipStream_t stream, bool dry) {
     if (bm == 256 && bn == 256) {
-        if constexpr ((FMT == kFmtQ4_K || FMT == kFmtQ5_K) && !XF32) {
-            if (dry) return hipSuccess;
-            hipLaunchKernelGGL(gemm_q4k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
-            return hipGetLastError();
-        } else if constexpr (FMT == kFmtQ6_K && !XF32) {
-            if (dry) return hipSuccess;
-            hipLaunchKernelGGL(gemm_q6k_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream, a);
-            return hipGetLastError();
-        } else if constexpr ((FMT == kFmtQ8_0 || FMT == kFmtQ4_0 || FMT == kFmtQ5_0 ||
-                              FMT == kFmtQ5_1) && !XF32) {
-            if (a.K % 256 == 0) {   // rows of whole 8-block runs: 16-byte aligned
-                if (dry) return hipSuccess;
-                hipLaunchKernelGGL(gemm_b32_rb_kernel<FMT>, dim3(grid), dim3(kThreads), 0, stream,
-                                   a);
-                return hipGetLastError();
-            }
-            return launch_tile<256, 256, FMT, XF32>(a, grid, stream, dry);
-        } else if constexpr (!XF32) {
-            return launch_tile<256, 256, FMT, XF32>(a, grid, stream, dry);
+        if constexpr (!XF32 && FMT != kFmtF16) {
+            if (hipError_t e = launch_rb<FMT, 256>(a, grid, stream, dry); e != hipErrorNotSupported)
+                return e;
         }
+        if constexpr (!XF32) return launch_tile<256, 256, FMT, XF32>(a, grid, stream, dry);
     } else if (bm == 256 && bn == 128) {
         return launch_tile<256, 128, FMT, XF32>(a, grid, stream, dry);
     } else if (bm == 128 && bn == 128) {
@@ -1085,10 +1120,9 @@ hipError_t launch_gemm_t(int fmt, const void *X, int ldx, const void *W, int64_t
     }
     if (e != hipSuccess || plan.split == 1 || dry) return e;
     const int blocks = plan.tail_tiles * (plan.bm * plan.bn / 1024);
-    hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, stream, ws, plan.split,
-                       plan.tail_tiles, plan.dp_tiles, plan.bm, plan.bn, plan.tiles_m,
-                       plan.tiles_n, Y, ldy, M, N);
-    return hipGetLastError();
+    return launch_splitk_reduce(plan.split, dim3(blocks), stream, ws, plan.tail_tiles,
+                                plan.dp_tiles, plan.bm, plan.bn, plan.tiles_m, plan.tiles_n, Y,
+                                ldy, M, N);
 }
 
 }  // namespace

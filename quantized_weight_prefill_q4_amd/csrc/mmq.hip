@@ -750,10 +750,9 @@ hipError_t launch_mmq(int fmt, const int8_t *Xq, int ldq, const float *ds, const
     }
     if (e != hipSuccess || plan.split == 1) return e;
     const int blocks = plan.tail_tiles * (plan.bm * plan.bn / 1024);
-    hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, stream, ws, plan.split,
-                       plan.tail_tiles, plan.dp_tiles, plan.bm, plan.bn, plan.tiles_m,
-                       plan.tiles_n, Y, ldy, M, N);
-    return hipGetLastError();
+    return launch_splitk_reduce(plan.split, dim3(blocks), stream, ws, plan.tail_tiles,
+                                plan.dp_tiles, plan.bm, plan.bn, plan.tiles_m, plan.tiles_n, Y,
+                                ldy, M, N);
 }
 
 }  // namespace mq

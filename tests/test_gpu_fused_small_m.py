@@ -1,0 +1,61 @@
+"""The fused GEMM at small M (<= 128; 64- and 128-row tiles), every format.
+
+* random inputs, no K split: bit-identical to the f16-cache GEMM (same
+  operands, same k order per output) and within the oracle's tolerance on
+  sampled rows;
+* integer inputs with forced K splits (ranges rounded to super-blocks or
+  step pairs, the last one ragged): exact.
+M and N are ragged against the tiles (M = 37, 100; N = 1000 is 3 full tiles
+and one of 232 rows)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import announce, check_gemm, needs_gpu, to_dev_f16, to_dev_u8, to_host
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+import quantized_weight_prefill_q4_amd as mq  # noqa: E402
+import torch  # noqa: E402
+
+FMT_NAME = {12: "Q4_K", 14: "Q6_K", 8: "Q8_0", 2: "Q4_0", 6: "Q5_0", 7: "Q5_1", 13: "Q5_K"}
+FMTS = (12, 13, 14, 8, 2, 6, 7)
+
+
+@pytest.mark.parametrize("M", [1, 37, 64, 65, 100, 128])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_small_m_random_equals_cache(fmt, M):
+    N, K = 1000, 2048
+    p = mq.gemm_plan(fmt, M, N, K, 1)
+    assert p["bm"] == (64 if M <= 64 else 128) and p["has_kernel"]
+    q = synth.weights(fmt, synth.rng(70, M, fmt, N), N, K)
+    x = synth.activations(synth.rng(70, M, role=1), M, K)
+    qd, xd = to_dev_u8(q), to_dev_f16(x)
+    announce("small-M fused vs cache", FMT_NAME[fmt], f"M={M}", f"N={N}", f"K={K}")
+    cache = mq.dequant_to_f16(qd, fmt, N, K)
+    yc = mq.gemm_f16cache(xd, cache, K, split_k=1)
+    yf = mq.gemm_fused(xd, qd, fmt, N, K, split_k=1)
+    ya = mq.gemm_fused(xd, qd, fmt, N, K)            # the automatic plan (K split)
+    torch.cuda.synchronize()
+    assert torch.equal(yc, yf), "fused and cache GEMMs differ at split 1"
+    rows = np.unique(np.array([0, M // 2, M - 1]))
+    w = oracle.dequant_ref(fmt, q, N, K)
+    check_gemm(to_host(yf)[rows], x, w, K, f"fused {FMT_NAME[fmt]} M={M}", rows=rows)
+    check_gemm(to_host(ya)[rows], x, w, K, f"fused {FMT_NAME[fmt]} M={M} auto split", rows=rows)
+
+
+@pytest.mark.parametrize("split", [0, 2, 3, 5, 16])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_small_m_integer_exact_with_splits(fmt, split):
+    M, N, K = 100, 1000, 3584 if fmt in (12, 13, 14) else 3840
+    q = synth.weights(fmt, synth.rng(71, split, fmt, N), N, K, mode="integer")
+    x = synth.activations(synth.rng(71, split, role=1), M, K, mode="integer")
+    p = mq.gemm_plan(fmt, M, N, K, split)
+    announce("small-M fused integer", FMT_NAME[fmt], f"M={M}", f"N={N}", f"K={K}",
+             f"split={split}", f"plan={p['bm']}x{p['bn']}/{p['split']}x{p['steps_per_split']}")
+    Y = to_host(mq.gemm_fused(to_dev_f16(x), to_dev_u8(q), fmt, N, K, split_k=split))
+    rows = np.array([0, 1, 31, 32, 63, 64, 98, 99])
+    Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(fmt, q, N, K))
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)

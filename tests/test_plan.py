@@ -48,9 +48,10 @@ def _check(p, fmt, M, N, K, split_k, path):
         assert (split - 1) * per < p["k_steps"] <= split * per
         if split_k >= 2:
             assert split <= split_k and p["dp_tiles"] == 0
-        q = fmt in ("q4_k", "q5_k") and bm == 256 and bn == 256
-        pairs = fmt == "q6_k" or (fmt in ("q8_0", "q4_0", "q5_0", "q5_1") and bm == 256
-                                  and bn == 256 and K % 256 == 0)
+        # the register-expansion kernels (256-column fused tiles)
+        q = fmt in ("q4_k", "q5_k") and bn == 256
+        pairs = fmt == "q6_k" or (fmt in ("q8_0", "q4_0", "q5_0", "q5_1") and bn == 256
+                                  and K % 256 == 0)
         if path == "f16" and q:
             assert per % 4 == 0, "Q4_K/Q5_K 256x256 ranges are whole super-blocks"
         elif path == "f16" and pairs:
