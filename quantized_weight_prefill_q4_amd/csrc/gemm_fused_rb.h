@@ -338,13 +338,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
         step(std::integral_constant<int, 3>(), kt + 3);
     }
 
-    // the 16-byte-store epilogue's patches: the X stages when they are large
-    // enough (256 rows), else the raw-weight buffers (idle after the loop too)
-    if constexpr (BM == 256)
-        store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
-    else
-        store_tile<BM, BN, FM, FN, TM, TN, (int)sizeof(Bq0)>(a, acc, tail, part, tile, m0, n0, wm,
-                                                             wn, lane, wave, Bq0, Bq1);
+    store_tile<BM, BN, FM, FN, TM, TN, 4, (int)sizeof(A0), (int)sizeof(Bq0)>(
+        a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1, Bq0, Bq1);
 }
 
 // ---------------------------------------------------------------------------
@@ -587,13 +582,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
         step(std::integral_constant<int, 0>(), kt);
         step(std::integral_constant<int, 1>(), kt + 1);
     }
-    // the 16-byte-store epilogue's patches: the X stages when they are large
-    // enough (256 rows), else the raw-weight buffers (idle after the loop too)
-    if constexpr (BM == 256)
-        store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
-    else
-        store_tile<BM, BN, FM, FN, TM, TN, (int)sizeof(Bq0)>(a, acc, tail, part, tile, m0, n0, wm,
-                                                             wn, lane, wave, Bq0, Bq1);
+    store_tile<BM, BN, FM, FN, TM, TN, 4, (int)sizeof(A0), (int)sizeof(Bq0)>(
+        a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1, Bq0, Bq1);
 }
 
 
@@ -904,13 +894,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
         step(std::integral_constant<int, 0>(), kt);
         step(std::integral_constant<int, 1>(), kt + 1);
     }
-    // the 16-byte-store epilogue's patches: the X stages when they are large
-    // enough (256 rows), else the raw-weight buffers (idle after the loop too)
-    if constexpr (BM == 256)
-        store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
-    else
-        store_tile<BM, BN, FM, FN, TM, TN, (int)sizeof(Bq0)>(a, acc, tail, part, tile, m0, n0, wm,
-                                                             wn, lane, wave, Bq0, Bq1);
+    store_tile<BM, BN, FM, FN, TM, TN, 4, (int)sizeof(A0), (int)sizeof(Bq0)>(
+        a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1, Bq0, Bq1);
 }
 
 }  // namespace

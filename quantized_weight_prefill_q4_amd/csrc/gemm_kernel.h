@@ -742,13 +742,14 @@ __device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x1
 // partial tile to slot (part, tail tile) of the workspace.  C layout of a
 // 32x32 MFMA block: the lane holds column (lane & 31) and rows
 // 8·(r/4) + 4·(lane/32) + r%4 for accumulator element r; rows and columns of
-// a partial tile past M/N hold zeros.  S0, S1: two LDS buffers of PATCH
-// bytes each, idle once the k-loop is done (by default the workgroup's two X
-// stages).
-template <int BM, int BN, int FM, int FN, int TM, int TN, int PATCH = BM * 8 * 16>
+// a partial tile past M/N hold zeros.  S0, S1 (SA bytes each) and S2, S3 (SB
+// bytes each): LDS buffers of the workgroup that are idle once the k-loop is
+// done (its X and weight stages); NW: waves per workgroup.
+template <int BM, int BN, int FM, int FN, int TM, int TN, int NW, int SA, int SB>
 __device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN], bool tail,
                                            int part, int tile, int m0, int n0, int wm, int wn,
-                                           int lane, int wave, u32x4 *S0, u32x4 *S1) {
+                                           int lane, int wave, u32x4 *S0, u32x4 *S1, u32x4 *S2,
+                                           u32x4 *S3) {
     float *out;
     int64_t ldo;
     int rows, cols;
@@ -764,15 +765,32 @@ __device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN],
         cols = a.N - n0;
     }
     const int col_l = lane & 31, row_l = (lane >> 5) * 4;
-    constexpr int PS = 36;   // patch row stride in floats (keeps 16-byte rows)
-    if constexpr (BM >= 64 && 4 * 32 * PS * 4 <= PATCH) {
+    constexpr int PS = 36;                 // patch row stride in floats (keeps 16-byte rows)
+    constexpr int PB = 32 * PS * 4;        // bytes of one wave's patch
+    constexpr int PA = SA / PB, PBB = SB / PB;   // patches in each S0/S1 and S2/S3
+    if constexpr (2 * (PA + PBB) >= NW) {
         // Full tile, 16-byte-aligned rows: each 32x32 block goes through a
-        // private 32 x 36-float LDS patch of the wave (waves 0-3 in S0, 4-7
-        // in S1, both idle after the last step) so that every lane then
+        // private 32 x 36-float LDS patch of the wave (the waves' patches are
+        // dealt over S0, S1, S2, S3 in that order) so that every lane then
         // stores 4 consecutive columns of one row — a quarter of the store
         // instructions of the column-per-lane layout.
         if (rows >= BM && cols >= BN && (ldo & 3) == 0) {
-            float *patch = reinterpret_cast<float *>(wave < 4 ? S0 : S1) + (wave & 3) * (32 * PS);
+            u32x4 *buf;
+            int slot;
+            if (wave < PA) {
+                buf = S0;
+                slot = wave;
+            } else if (wave < 2 * PA) {
+                buf = S1;
+                slot = wave - PA;
+            } else if (wave < 2 * PA + PBB) {
+                buf = S2;
+                slot = wave - 2 * PA;
+            } else {
+                buf = S3;
+                slot = wave - 2 * PA - PBB;
+            }
+            float *patch = reinterpret_cast<float *>(buf) + slot * (32 * PS);
             sync_lds();              // every wave is done reading the stages
             const int rr = lane >> 3, cc = 4 * (lane & 7);
 #pragma unroll
@@ -956,7 +974,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     }
     if (kt < kt_end) step(std::integral_constant<int, 0>(), kt);
 
-    store_tile<BM, BN, FM, FN, TM, TN>(a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1);
+    store_tile<BM, BN, FM, FN, TM, TN, NWV, BM * CPR * 16, BN * CPR * 16>(
+        a, acc, tail, part, tile, m0, n0, wm, wn, lane, wave, A0, A1, B0, B1);
 }
 
 }  // namespace

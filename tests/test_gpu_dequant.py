@@ -15,7 +15,7 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 
 import quantized_weight_prefill_q4_amd as mq  # noqa: E402
 
-FMT_NAME = {12: "Q4_K", 14: "Q6_K", 8: "Q8_0"}
+FMT_NAME = {12: "Q4_K", 14: "Q6_K", 8: "Q8_0", 2: "Q4_0", 6: "Q5_0", 7: "Q5_1", 13: "Q5_K"}
 
 
 def _run(fmt, q, N, K, pad):
@@ -121,14 +121,15 @@ def test_real_shapes_full(name, fmt, N, K):
 
 
 def test_batch_matches_oracle_across_launches():
-    """mq_dequant_to_f16_batch: 21 jobs of all three formats, padded and
-    unpadded, odd row counts — two kernel launches (16 + 5 jobs) with
+    """mq_dequant_to_f16_batch: 28 jobs of all seven formats, padded and
+    unpadded, odd row counts — two kernel launches (16 + 12 jobs) with
     workgroups of different jobs and formats in one grid.  Every cache must
     equal the oracle's bit for bit, pad columns +0."""
     shapes = [(12, 3, 256), (14, 5, 512), (8, 7, 96), (12, 130, 2048), (14, 65, 1024),
-              (8, 300, 4096), (12, 1, 4096), (14, 2, 256), (8, 33, 32), (12, 17, 3584)]
+              (8, 300, 4096), (12, 1, 4096), (14, 2, 256), (8, 33, 32), (12, 17, 3584),
+              (2, 11, 512), (6, 9, 2080), (7, 4, 1024), (13, 6, 512)]
     jobs, exp = [], []
-    for i in range(21):
+    for i in range(28):
         fmt, N, K = shapes[i % len(shapes)]
         pad = i % 3 != 1
         q = synth.weights(fmt, synth.rng(40, 0, fmt, i), N, K)
