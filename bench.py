@@ -4,11 +4,15 @@
 Workload (the timed step): one prefill forward's matmuls over a full 28-layer
 7B weight set — per layer q, o (3584×3584), k, v (512×3584), gate, up
 (18944×3584) in Q4_K and down (3584×18944) in Q6_K — at M = 2048 tokens with
-f16 N(0,1) activations, 196 GEMMs Y = X·Wᵀ on the persistent f16 cache.
-Before the steps, the load phase decodes all 196 weights into the cache
-(the method's one-time dequant; timed, reported as GB/s).  After them, the
-fused dequant-in-GEMM is timed on the same forward, and the fused-vs-cache
-crossover in M is swept on Llama-3.1-8B-like shapes.
+f16 N(0,1) activations, Y = X·Wᵀ on the persistent f16 cache.  The weights
+that share an input are stored and cached as one matrix each (q|k|v, N = 4608;
+gate|up, N = 37888; Fucina "Eager GPU Offload Without A Compute Graph",
+quantized linears: a shared-input batch), so a step is 112 GEMMs that compute
+the 196 products; the same forward as 196 single GEMMs (row views of the same
+caches) is timed beside it.  Before the steps, the load phase decodes all 196
+weights into the cache (the method's one-time dequant; timed, reported as
+GB/s).  After them, the fused dequant-in-GEMM is timed on the same forward,
+and the fused-vs-cache crossover in M is swept on Llama-3.1-8B-like shapes.
 
 Inputs are synthetic and seeded (the pages' real GGUF models are not
 available): the 4.2 GB weight set is drawn on the device with torch's seeded
@@ -36,15 +40,18 @@ import synth  # noqa: E402
 METRIC = "prefill GEMM TFLOP/s + matmul tok/s (7B Q4_K, M=2048); dequant GB/s"
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense f16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-# The dominant kernel of the step: the gate and up GEMMs (2 x 28 of the 196
-# calls, ~60% of the matmul time), i.e. gemm_kernel<256, 256, f16> plus the
-# fixed-order reduce of its K-split tail tiles (one mq_gemm_f16cache call).
-ROOFLINE_SHAPES = ("gate", "up")
-ROOFLINE_KERNEL = "gemm_kernel<256, 256, f16> + splitk_reduce (mq_gemm_f16cache, gate/up 18944x3584)"
+# The dominant kernel of the step: the grouped gate|up GEMM (28 of the 112
+# calls, ~58% of the matmul time): gemm_kernel<256, 256, f16> on 1184 whole
+# tiles (one mq_gemm_f16cache call, no K split).
+ROOFLINE_GROUP = "gu"
+ROOFLINE_N, ROOFLINE_K = 37888, 3584
+ROOFLINE_KERNEL = "gemm_kernel<256, 256, f16> (mq_gemm_f16cache, gate|up 37888x3584, 1184 whole tiles)"
 # Measured HBM traffic of that call (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
 # by a plain copy of known size) with the hash of the GEMM source it was taken
 # on; reported only while the source is unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_f16cache_gate_7b_m2048_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_f16cache_gateup_7b_m2048_traffic.md")
+# Shared-input groups of a layer: (group, member matrices in row order)
+GROUPS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gu", ("gate", "up")), ("down", ("down",)))
 GEMM_SOURCES = ("quantized_weight_prefill_q4_amd/csrc/gemm_kernel.h",
                 "quantized_weight_prefill_q4_amd/csrc/gemm_fused_rb.h",
                 "quantized_weight_prefill_q4_amd/csrc/gemm.hip",
@@ -65,7 +72,7 @@ def parse():
     p.add_argument("--load-reps", type=int, default=3)
     p.add_argument("--fused-steps", type=int, default=5)
     p.add_argument("--grouped-steps", type=int, default=5,
-                   help="steps of the grouped forward (q|k|v, gate|up as one GEMM each); 0 = skip")
+                   help="steps of the fused grouped forward (q|k|v, gate|up as one GEMM each); 0 = skip")
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-formats", action="store_true",
                    help="skip the per-format decode / fused table")
@@ -79,7 +86,7 @@ def parse():
     p.add_argument("--cpu-layers", type=int, default=4,
                    help="layers (7 matrices each) of the oracle sample")
     p.add_argument("--only-shape", default=None,
-                   help="profiling aid: run only this 7B matrix's cache GEMM --steps times")
+                   help="profiling aid: run only this 7B matrix's (or group qkv, gate_up) cache GEMM --steps times")
     p.add_argument("--only-fused", default=None,
                    help="profiling aid: run only this 7B matrix's fused GEMM --steps times")
     p.add_argument("--only-mmq", default=None,
@@ -129,7 +136,9 @@ def measured_traffic():
 
 
 def run_only_shape(torch, mq, name, steps, dev):
-    fmt, N, K = next((f, n, k) for nm, f, n, k in synth.LAYER_7B if nm == name)
+    shapes = {nm: (f, n, k) for nm, f, n, k in synth.LAYER_7B}
+    shapes.update(qkv=(synth.Q4_K, 4608, 3584), gate_up=(synth.Q4_K, 37888, 3584))
+    fmt, N, K = shapes[name]
     M = 2048
     q = synth.weights_device(fmt, 1, N, K, dev)
     cache = mq.dequant_to_f16(q, fmt, N, K)
@@ -213,17 +222,30 @@ def run_calib_copy(torch, steps, dev):
 # ---------------------------------------------------------------------------
 
 def make_weights(torch, mq, layers, dev):
-    """Quantized weights on the device plus their (empty) f16 caches."""
-    W = []
+    """Quantized weights on the device plus their (empty) f16 caches, per
+    layer and shared-input group (GROUPS) one buffer each, the matrices row
+    slices of it.  Returns (W, G): W[layer][matrix] = (fmt, N, K, q, cache)
+    with views, G[layer][group] = (fmt, N, K, q, cache) with the buffers."""
+    W, G = [], []
+    spec = {name: (mi, fmt, N, K) for mi, (name, fmt, N, K) in enumerate(synth.LAYER_7B)}
     for L in range(layers):
-        row = {}
-        for mi, (name, fmt, N, K) in enumerate(synth.LAYER_7B):
-            q = synth.weights_device(fmt, 1000 * L + mi, N, K, dev)
-            cache = torch.empty((N, mq.cache_ld(K)), dtype=torch.float16, device=dev)
-            row[name] = (fmt, N, K, q, cache)
-        W.append(row)
+        row, grp = {}, {}
+        for gname, members in GROUPS:
+            fmt, K = spec[members[0]][1], spec[members[0]][3]
+            n_tot = sum(spec[m][2] for m in members)
+            qbuf = torch.empty((n_tot, mq.row_bytes(fmt, K)), dtype=torch.uint8, device=dev)
+            cbuf = torch.empty((n_tot, mq.cache_ld(K)), dtype=torch.float16, device=dev)
+            r0 = 0
+            for m in members:
+                mi, f, N, _ = spec[m]
+                qbuf[r0:r0 + N] = synth.weights_device(f, 1000 * L + mi, N, K, dev)
+                row[m] = (f, N, K, qbuf[r0:r0 + N], cbuf[r0:r0 + N])
+                r0 += N
+            grp[gname] = (fmt, n_tot, K, qbuf, cbuf)
+        W.append({m: row[m] for m, *_ in synth.LAYER_7B})
+        G.append(grp)
     torch.cuda.synchronize()
-    return W
+    return W, G
 
 
 def load_phase(torch, mq, W, reps):
@@ -268,6 +290,16 @@ def forward(mq, W, xa, xf, ys, ws, events=None, only=None):
             i += 1
     if events is not None:
         events[i].record()
+
+
+def forward_grouped(mq, G, xa, xf, yg, ws, only=None):
+    """One prefill forward as 4 GEMMs per layer (q|k|v, o, gate|up, down);
+    with `only`, just the calls of those groups."""
+    for grp in G:
+        for gname, (fmt, N, K, q, cache) in grp.items():
+            if only is not None and gname not in only:
+                continue
+            mq.gemm_f16cache(xf if gname == "down" else xa, cache, K, out=yg[gname], ws=ws)
 
 
 def forward_fused(mq, W, xa, xf, ys, ws):
@@ -582,64 +614,14 @@ def vendor_table(torch, W, xa, xf, shape_us, reps=20):
     return out
 
 
-def grouped_forward(torch, mq, W, xa, xf, steps, dev):
-    """The forward with the shared-input GEMMs grouped: per layer one q|k|v GEMM
-    (N = 4608), o, one gate|up GEMM (N = 37888) and down — 112 calls instead of
-    196.  The grouped caches are decoded by one batched call straight into row
-    slices of one buffer per group; the products are the same.  Returns
-    (median ms per step, min ms per step)."""
-    M = xa.shape[0]
-    groups = []
-    jobs = []
-    for row in W:
-        qkv = torch.empty((3584 + 512 + 512, 3584), dtype=torch.float16, device=dev)
-        gu = torch.empty((2 * 18944, 3584), dtype=torch.float16, device=dev)
-        r0 = 0
-        for name in ("q", "k", "v"):
-            fmt, N, K, q, _ = row[name]
-            jobs.append((q, fmt, N, K, qkv[r0:r0 + N]))
-            r0 += N
-        r0 = 0
-        for name in ("gate", "up"):
-            fmt, N, K, q, _ = row[name]
-            jobs.append((q, fmt, N, K, gu[r0:r0 + N]))
-            r0 += N
-        groups.append((qkv, row["o"][4], gu, row["down"][4]))
-    mq.dequant_to_f16_batch(jobs)
-    y_qkv = torch.empty((M, 4608), dtype=torch.float32, device=dev)
-    y_o = torch.empty((M, 3584), dtype=torch.float32, device=dev)
-    y_gu = torch.empty((M, 37888), dtype=torch.float32, device=dev)
-    y_d = torch.empty((M, 3584), dtype=torch.float32, device=dev)
-    wsb = max(mq.workspace_bytes(0, M, N, K) for N, K in ((4608, 3584), (3584, 3584), (37888, 3584), (3584, 18944)))
-    ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
-
-    def step():
-        for qkv, o, gu, down in groups:
-            mq.gemm_f16cache(xa, qkv, 3584, out=y_qkv, ws=ws)
-            mq.gemm_f16cache(xa, o, 3584, out=y_o, ws=ws)
-            mq.gemm_f16cache(xa, gu, 3584, out=y_gu, ws=ws)
-            mq.gemm_f16cache(xf, down, 18944, out=y_d, ws=ws)
-
-    step()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    for i in range(steps):
-        evs[i].record()
-        step()
-    evs[steps].record()
-    torch.cuda.synchronize()
-    d = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    del groups, jobs
-    return statistics.median(d), min(d)
-
-
 FWD_ROWS = 64     # token rows of the timed forward's output sample
 FWD_COLS = 256    # output columns (weight rows) per matrix
 
 
-def forward_sample(torch, W, xa, xf, ys, M):
+def forward_sample(torch, G, xa, xf, yg, M):
     """Host copy of part of what the last timed forward computed: for each of
-    the last layer's seven GEMMs (every call of a shape writes the same output
-    buffer, layer by layer, so the buffers hold layer 27's products),
+    the last layer's four grouped GEMMs (every call of a group writes the same
+    output buffer, layer by layer, so the buffers hold layer 27's products),
     FWD_ROWS token rows x FWD_COLS output columns of Y, the same rows of X,
     and the quantized bytes and f16-cache rows of the FWD_COLS weight rows.
     Rows and columns are seeded draws that include the first and the last."""
@@ -652,14 +634,13 @@ def forward_sample(torch, W, xa, xf, ys, M):
         return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
     out = {"rows": rows, "x": {"a": bits(xa[ridx]), "f": bits(xf[ridx])}, "mats": {}}
-    for name, (fmt, N, K, q, cache) in W[-1].items():
+    for name, (fmt, N, K, q, cache) in G[-1].items():
         cols = np.sort(np.concatenate([[0, N - 1], 1 + g.choice(N - 2, FWD_COLS - 2, replace=False)]))
         cidx = torch.from_numpy(cols).to(xa.device)
-        rb = q.numel() // N
         out["mats"][name] = {
             "fmt": fmt, "N": N, "K": K, "cols": cols,
-            "y": ys[name][ridx][:, cidx].cpu().numpy(),
-            "q": q.view(N, rb)[cidx].cpu().numpy(),
+            "y": yg[name][ridx][:, cidx].cpu().numpy(),
+            "q": q[cidx].cpu().numpy(),
             "cache": bits(cache[cidx, :K]),
         }
     return out
@@ -691,34 +672,21 @@ def check_forward_sample(sample):
             "pass": bool(cache_ok and worst <= 1.0)}
 
 
-def fused_grouped_forward(torch, mq, W, xa, xf, steps, dev):
-    """The fused forward with the shared-input weights grouped: per layer the
-    quantized q, k and v rows (all Q4_K over K = 3584) copied into one
-    4608-row weight, gate and up into one 37888-row weight, then four fused
-    GEMMs per layer instead of seven (Fucina "Eager GPU Offload Without A
-    Compute Graph", quantized linears: a shared-input batch).  Returns
-    (median ms per step, min ms per step)."""
+def fused_grouped_forward(torch, mq, G, xa, xf, steps, dev):
+    """The fused forward on the grouped quantized weights (q|k|v as one
+    4608-row Q4_K weight, gate|up as one 37888-row weight: the rows of a group
+    are contiguous blocks of one format), four fused GEMMs per layer.
+    Returns (median ms per step, min ms per step)."""
     M = xa.shape[0]
-    groups = []
-    for row in W:
-        qkv = torch.cat([row[n][3] for n in ("q", "k", "v")])
-        gu = torch.cat([row[n][3] for n in ("gate", "up")])
-        groups.append((qkv, row["o"], gu, row["down"]))
-    y_qkv = torch.empty((M, 4608), dtype=torch.float32, device=dev)
-    y_o = torch.empty((M, 3584), dtype=torch.float32, device=dev)
-    y_gu = torch.empty((M, 37888), dtype=torch.float32, device=dev)
-    y_d = torch.empty((M, 3584), dtype=torch.float32, device=dev)
-    q4k, q6k = mq.FORMATS["q4_k"], mq.FORMATS["q6_k"]
-    wsb = max(mq.workspace_bytes(q4k, M, 4608, 3584), mq.workspace_bytes(q4k, M, 3584, 3584),
-              mq.workspace_bytes(q4k, M, 37888, 3584), mq.workspace_bytes(q6k, M, 3584, 18944))
+    yg = {g: torch.empty((M, N), dtype=torch.float32, device=dev)
+          for g, (f, N, K, q, c) in G[0].items()}
+    wsb = max(mq.workspace_bytes(f, M, N, K) for f, N, K, q, c in G[0].values())
     ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
 
     def step():
-        for qkv, o, gu, down in groups:
-            mq.gemm_fused(xa, qkv, q4k, 4608, 3584, out=y_qkv, ws=ws)
-            mq.gemm_fused(xa, o[3], o[0], 3584, 3584, out=y_o, ws=ws)
-            mq.gemm_fused(xa, gu, q4k, 37888, 3584, out=y_gu, ws=ws)
-            mq.gemm_fused(xf, down[3], down[0], 3584, 18944, out=y_d, ws=ws)
+        for grp in G:
+            for gname, (fmt, N, K, q, c) in grp.items():
+                mq.gemm_fused(xf if gname == "down" else xa, q, fmt, N, K, out=yg[gname], ws=ws)
 
     step()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -728,7 +696,7 @@ def fused_grouped_forward(torch, mq, W, xa, xf, steps, dev):
     evs[steps].record()
     torch.cuda.synchronize()
     d = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    del groups
+    del yg, ws
     return statistics.median(d), min(d)
 
 
@@ -971,7 +939,7 @@ def main():
         print(json.dumps({"crossover": cross}), flush=True)
         return
     if args.only_load:
-        W = make_weights(torch, mq, args.layers, dev)
+        W, _ = make_weights(torch, mq, args.layers, dev)
         jobs = [(q, fmt, N, K, cache) for row in W for fmt, N, K, q, cache in row.values()]
         for _ in range(args.steps):
             mq.dequant_to_f16_batch(jobs)
@@ -986,7 +954,7 @@ def main():
 
     # -- weights and the load phase (one-time dequant into the f16 cache) ------
     t0 = time.time()
-    W = make_weights(torch, mq, layers, dev)
+    W, G = make_weights(torch, mq, layers, dev)
     qbytes = sum(r[n][3].numel() for r in W for n in r)
     cbytes = sum(r[n][1] * r[n][2] * 2 for r in W for n in r)
     log(f"[bench] {layers * 7} weights drawn on device in {time.time() - t0:.1f}s: "
@@ -1016,61 +984,75 @@ def main():
     xa = synth.activations_device(7001, M, 3584, dev)
     xf = synth.activations_device(7002, M, 18944, dev)
     ys = {n: torch.empty((M, N), dtype=torch.float32, device=dev) for n, _, N, _ in synth.LAYER_7B}
-    ws_bytes = max(mq.workspace_bytes(0, M, N, K) for _, _, N, K in synth.LAYER_7B)
+    yg = {g: torch.empty((M, N), dtype=torch.float32, device=dev)
+          for g, (f, N, K, q, c) in G[0].items()}
+    ws_bytes = max([mq.workspace_bytes(0, M, N, K) for _, _, N, K in synth.LAYER_7B] +
+                   [mq.workspace_bytes(0, M, N, K) for f, N, K, q, c in G[0].values()])
     ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device=dev)
     calls = [(n, f, N, K) for row in W for n, (f, N, K, _, _) in row.items()]
+    gcalls = [(g, f, N, K) for grp in G for g, (f, N, K, _, _) in grp.items()]
+    flops_step = sum(2.0 * M * N * K for _, _, N, K in calls)
+    assert abs(flops_step - sum(2.0 * M * N * K for _, _, N, K in gcalls)) < 1.0
 
-    for _ in range(args.warmup):
-        forward(mq, W, xa, xf, ys, ws)
-    # The timed steps carry one HIP event per step boundary only: an event
-    # record before every call costs ~2% of the step by itself (measured
-    # 27.07 vs 27.60 ms), so the per-call durations come from a second pass
-    # of the same steps with events around every call.
-    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        bounds[s].record()
-        forward(mq, W, xa, xf, ys, ws)
-    bounds[args.steps].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_per_step = wall * 1e3 / args.steps
-    step_ms = [bounds[s].elapsed_time(bounds[s + 1]) for s in range(args.steps)]
-    ev_step_ms = statistics.median(step_ms)
-    min_step_ms = min(step_ms)
+    def timed_steps(step_fn):
+        """(wall ms per step, median and min event ms per step) over args.steps
+        steps after args.warmup untimed ones; one HIP event per step boundary."""
+        for _ in range(args.warmup):
+            step_fn()
+        bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for st in range(args.steps):
+            bounds[st].record()
+            step_fn()
+        bounds[args.steps].record()
+        torch.cuda.synchronize()
+        wall_ = time.perf_counter() - t0
+        d = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
+        return wall_ * 1e3 / args.steps, statistics.median(d), min(d)
 
-    # What the timed forward computed: a sample of the last layer's seven
-    # outputs (every call of a shape writes the same buffer, layer by layer),
-    # with the rows of X and of the weights it needs, for the oracle check of
-    # the CPU leg.  Untimed.
-    fwd_sample = forward_sample(torch, W, xa, xf, ys, M)
+    # the headline: the grouped forward (112 GEMMs computing the 196 products)
+    ms_per_step, ev_step_ms, min_step_ms = timed_steps(lambda: forward_grouped(mq, G, xa, xf, yg, ws))
+    # What the timed forward computed: a sample of the last layer's four
+    # grouped outputs with the rows of X and of the weights it needs, for the
+    # oracle check of the CPU leg.  Untimed.
+    fwd_sample = forward_sample(torch, G, xa, xf, yg, M)
+    # the same forward as 196 single GEMMs on row views of the same caches
+    f196_wall, f196_ev, f196_min = timed_steps(lambda: forward(mq, W, xa, xf, ys, ws))
 
     # Per-call GPU time per shape and of the roofline kernel: graph replays of
-    # the forward's calls of that shape (28 per step; gate and up together for
-    # the roofline), see graph_us.
+    # the forward's calls of that shape (28 per step), see graph_us.
     def shape_calls(names):
         return [lambda fmt=fmt, N=N, K=K, cache=cache, name=name:
                 mq.gemm_f16cache(xf if name == "down" else xa, cache, K, out=ys[name], ws=ws)
                 for row in W for name, (fmt, N, K, q, cache) in row.items() if name in names]
 
+    def group_calls(gname):
+        return [lambda N=N, K=K, cache=cache:
+                mq.gemm_f16cache(xf if gname == "down" else xa, cache, K, out=yg[gname], ws=ws)
+                for grp in G for g, (fmt, N, K, q, cache) in grp.items() if g == gname]
+
     shape_rows = []
     for n, f, N, K in synth.LAYER_7B:
         t_us = graph_us(torch, shape_calls((n,)), replays=5)
         shape_rows.append((n, N, K, t_us, 2.0 * M * N * K / t_us / 1e6))
-    avg_launch_us = graph_us(torch, shape_calls(ROOFLINE_SHAPES), replays=7)
-    ach = 2.0 * M * 18944 * 3584 / avg_launch_us / 1e6
-    flops = np.array([2.0 * M * N * K for _, _, N, K in calls])
+    group_rows = []
+    for g, (f, N, K, q, c) in G[0].items():
+        t_us = graph_us(torch, group_calls(g), replays=7 if g == ROOFLINE_GROUP else 5)
+        group_rows.append((g, N, K, t_us, 2.0 * M * N * K / t_us / 1e6))
+    avg_launch_us = next(t for g, N, K, t, tf in group_rows if g == ROOFLINE_GROUP)
+    ach = 2.0 * M * ROOFLINE_N * ROOFLINE_K / avg_launch_us / 1e6
     traffic, traffic_note = measured_traffic()
-    gemm_tflops = float(flops.sum() / (ev_step_ms / 1e3) / 1e12)
-    tok_s = M * args.steps / wall
-    log(f"[bench] forward: {ms_per_step:.3f} ms/step wall, {ev_step_ms:.3f} ms in events, "
-        f"{tok_s:.0f} matmul tok/s, {gemm_tflops:.0f} TFLOP/s over {len(calls)} GEMMs; "
-        f"per call (graph replays of each shape's 28 calls):")
-    for n, N, K, t_us, tf in shape_rows:
+    gemm_tflops = flops_step / (ev_step_ms / 1e3) / 1e12
+    tok_s = M / (ms_per_step / 1e3)
+    log(f"[bench] forward (4 grouped GEMMs per layer, {len(gcalls)} calls): {ms_per_step:.3f} ms/step wall, "
+        f"{ev_step_ms:.3f} ms in events, {tok_s:.0f} matmul tok/s, {gemm_tflops:.0f} TFLOP/s; "
+        f"as 196 single GEMMs: {f196_ev:.3f} ms/step ({M / (f196_ev / 1e3):.0f} tok/s)")
+    log("    per call (graph replays of each shape's 28 calls):")
+    for n, N, K, t_us, tf in group_rows + shape_rows:
         log(f"    {n:5s} {N:6d}x{K:<6d} {t_us:9.1f} us  {tf:7.1f} TFLOP/s  "
             f"({100 * tf / PEAK_F16_TFLOPS:.1f}% of peak)")
-    log(f"[bench] roofline kernel ({ROOFLINE_KERNEL}, {2 * layers} calls/step): "
+    log(f"[bench] roofline kernel ({ROOFLINE_KERNEL}, {layers} calls/step): "
         f"{ach:.0f} TFLOP/s = {100 * ach / PEAK_F16_TFLOPS:.1f}% of {PEAK_F16_TFLOPS:.0f}, "
         f"avg call {avg_launch_us:.1f} us; traffic {traffic} B/call ({traffic_note})")
 
@@ -1078,14 +1060,14 @@ def main():
     # Once over the whole step, once over the roofline kernel's calls alone
     # (the gate/up GEMMs draw more power than the step's average).
     clock = None
-    c_fwd = clock_sample(torch, lambda: forward(mq, W, xa, xf, ys, ws))
-    c_dom = clock_sample(torch, lambda: forward(mq, W, xa, xf, ys, ws, only=ROOFLINE_SHAPES))
+    c_fwd = clock_sample(torch, lambda: forward_grouped(mq, G, xa, xf, yg, ws))
+    c_dom = clock_sample(torch, lambda: forward_grouped(mq, G, xa, xf, yg, ws, only=(ROOFLINE_GROUP,)))
     if c_fwd is not None and c_dom is not None:
         at = PEAK_F16_TFLOPS * c_dom["sclk_mhz_median"] / 2400.0
         clock = {"forward": c_fwd, "roofline_kernel": c_dom,
                  "mfma_peak_at_kernel_sclk_tflops": round(at, 1),
                  "roofline_frac_at_kernel_sclk": round(ach / at, 4)}
-        for what, c in (("the forward", c_fwd), ("gate/up calls only", c_dom)):
+        for what, c in (("the forward", c_fwd), ("gate|up calls only", c_dom)):
             log(f"[bench] clock during {what}: {c['sclk_mhz_median']} MHz median "
                 f"({c['sclk_mhz_min']}-{c['sclk_mhz_max']}), socket power "
                 f"{c['socket_power_w_median']} W of {c['power_cap_w']} W cap")
@@ -1097,23 +1079,12 @@ def main():
     log("[bench] vendor library (torch.mm / hipBLASLt, f16 out) vs this library (f32 out), M = 2048: " +
         ", ".join(f"{n} {v['vendor_us']:.1f} vs {v['ours_us']:.1f} us" for n, v in vendor.items()))
 
-    # -- grouped shared-input forward (q|k|v and gate|up as one GEMM each) ------------
-    grouped = None
-    if args.grouped_steps > 0:
-        g_med, g_min = grouped_forward(torch, mq, W, xa, xf, args.grouped_steps, dev)
-        grouped = {"ms_per_step_median": round(g_med, 3), "ms_per_step_min": round(g_min, 3),
-                   "tok_s": round(M / (g_med / 1e3), 1),
-                   "tflops": round(flops.sum() / (g_med / 1e3) / 1e12, 1), "gemms_per_step": 4 * layers}
-        log(f"[bench] grouped forward (4 GEMMs per layer): {g_med:.3f} ms/step median, "
-            f"{grouped['tok_s']:.0f} tok/s, {grouped['tflops']:.0f} TFLOP/s")
-        torch.cuda.empty_cache()
-
     # -- int8 (MMQ) forward ----------------------------------------------------------
     mmqf = None
     if args.mmq_steps > 0:
         m_ms, q_ms = mmq_forward(torch, mq, W, M, args.mmq_steps, dev)
         mmqf = {"ms_per_step": round(m_ms, 3), "tok_s": round(M / (m_ms / 1e3), 1),
-                "tops": round(flops.sum() / (m_ms / 1e3) / 1e12, 1),
+                "tops": round(flops_step / (m_ms / 1e3) / 1e12, 1),
                 "quantize_ms_per_step": round(q_ms, 3)}
         log(f"[bench] int8 (MMQ) forward: {m_ms:.3f} ms/step, {mmqf['tok_s']:.0f} tok/s, "
             f"{mmqf['tops']:.0f} TOP/s (of which {q_ms:.3f} ms quantizing activations)")
@@ -1133,13 +1104,13 @@ def main():
         # element expansions: each weight element once per row tile of its plan
         expn = sum(-(-M // mq.gemm_plan(f, M, N, K)["bm"]) * N * K for _, f, N, K in calls)
         fused = {"ms_per_step": round(f_ms, 3), "tok_s": round(M / (f_ms / 1e3), 1),
-                 "tflops": round(flops.sum() / (f_ms / 1e3) / 1e12, 1),
+                 "tflops": round(flops_step / (f_ms / 1e3) / 1e12, 1),
                  "expansions_per_step": int(expn),
                  "expansions_per_s": round(expn / (f_ms / 1e3), 1)}
         log(f"[bench] fused forward: {f_ms:.3f} ms/step, {fused['tok_s']:.0f} tok/s, "
             f"{expn / (f_ms / 1e3) / 1e12:.2f} T element expansions/s")
         if args.grouped_steps > 0:
-            fg_med, fg_min = fused_grouped_forward(torch, mq, W, xa, xf, args.grouped_steps, dev)
+            fg_med, fg_min = fused_grouped_forward(torch, mq, G, xa, xf, args.grouped_steps, dev)
             fused["grouped_ms_per_step_median"] = round(fg_med, 3)
             fused["grouped_tok_s"] = round(M / (fg_med / 1e3), 1)
             log(f"[bench] fused grouped forward (4 GEMMs per layer): {fg_med:.3f} ms/step median, "
@@ -1149,7 +1120,7 @@ def main():
     # -- crossover sweep -------------------------------------------------------------
     cross = None
     if not args.no_sweep:
-        del W
+        del W, G
         torch.cuda.empty_cache()
         rows = []
         cross = sweep(torch, mq, dev, rows)
@@ -1208,24 +1179,32 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": ("7B prefill matmuls: 28 layers x {q,o 3584x3584, k,v 512x3584, "
-                         "gate,up 18944x3584 Q4_K; down 3584x18944 Q6_K}, f16 cache, M=2048"),
-            "M": M, "layers": layers, "gemms_per_step": len(calls),
+                         "gate,up 18944x3584 Q4_K; down 3584x18944 Q6_K}, f16 cache, M=2048; "
+                         "shared-input weights grouped (q|k|v N=4608, gate|up N=37888): "
+                         "112 GEMMs per step computing the 196 products"),
+            "M": M, "layers": layers, "gemms_per_step": len(gcalls), "products_per_step": len(calls),
             "quant_gb": round(qbytes / 1e9, 3), "cache_gb": round(cbytes / 1e9, 3),
         },
         "gemm_tflops": round(gemm_tflops, 1),
         "dequant_gbs": round(deq_gbs, 1),
         "dequant_ms": round(deq_ms, 3),
         "redequant_tok_s": round(M / ((ev_step_ms + deq_ms) / 1e3), 1),
-        "per_shape_tflops": {n: round(tf, 1) for n, _, _, _, tf in shape_rows},
+        "per_shape_tflops": {n: round(tf, 1) for n, _, _, _, tf in group_rows + shape_rows},
+        "per_shape_us": {n: round(t, 2) for n, _, _, t, _ in group_rows + shape_rows},
+        "forward_196": {"ms_per_step": round(f196_wall, 4), "ms_per_step_median_events": round(f196_ev, 4),
+                        "ms_per_step_min_events": round(f196_min, 4),
+                        "tok_s": round(M / (f196_ev / 1e3), 1),
+                        "tflops": round(flops_step / (f196_ev / 1e3) / 1e12, 1), "gemms_per_step": len(calls)},
         "roofline": {
             "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_F16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": traffic,
             "traffic_note": traffic_note,
             "kernel": ROOFLINE_KERNEL, "avg_launch_us": round(avg_launch_us, 2),
-            "timing": "HIP events around graph replays of the 56 gate/up calls of a step "
-                      "(GEMM + tail reduce per call; host launch gaps excluded)",
-            "launches_per_step": 2 * layers,
-            "algorithmic_bytes_per_call": M * 3584 * 2 + 18944 * 3584 * 2 + M * 18944 * 4,
+            "timing": "HIP events around graph replays of the 28 gate|up calls of a step "
+                      "(host launch gaps excluded)",
+            "launches_per_step": layers,
+            "flops_per_call": 2 * M * ROOFLINE_N * ROOFLINE_K,
+            "algorithmic_bytes_per_call": M * ROOFLINE_K * 2 + ROOFLINE_N * ROOFLINE_K * 2 + M * ROOFLINE_N * 4,
         },
         "clock": clock,
         "dequant_roofline": {
@@ -1237,7 +1216,6 @@ def main():
         "forward_check": fwd_check,
         "fused": fused,
         "mmq_forward": mmqf,
-        "grouped_forward": grouped,
         "vendor_gemm": vendor,
         "crossover": cross,
         "formats": fmts,

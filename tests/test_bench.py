@@ -87,8 +87,10 @@ def test_reduced_bench_prints_the_contract_line():
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
     assert cpu["dequant_parallel_gbs"] > 0 and cpu["dequant_parallel_procs"] >= 1
     fc = d["forward_check"]
-    assert fc["pass"] and fc["cache_bit_exact"] and fc["gemms"] == 7
-    assert fc["outputs_checked"] == 7 * 64 * 256
+    assert fc["pass"] and fc["cache_bit_exact"] and fc["gemms"] == 4
+    assert fc["outputs_checked"] == 4 * 64 * 256
+    assert d["config"]["gemms_per_step"] == 4 * 2 and d["config"]["products_per_step"] == 7 * 2
+    assert d["forward_196"]["ms_per_step"] > 0
     dq = d["dequant_roofline"]
     assert dq["hbm_copy_gbs"] > 0 and abs(dq["frac_of_copy"] - dq["achieved"] / dq["hbm_copy_gbs"]) < 1e-3
     assert d["fused"]["expansions_per_s"] > 0

@@ -244,3 +244,30 @@ def test_narrow_output_64_row_tiles_exact():
     Y, _ = _gemm(x, w, K)
     Yref, _ = oracle.gemm_ref(x, w)
     assert np.array_equal(Y.astype(np.float64), Yref)
+
+
+def test_grouped_fused_equals_per_matrix():
+    """The shared-input batch on the fused path: the quantized q, k, v rows of
+    a 7B layer (all Q4_K over K = 3584) placed one after another form one
+    4608-row weight, and gate and up one 37888-row weight.  One fused GEMM on
+    each group equals the per-matrix fused GEMMs column for column, bit for
+    bit at split 1 (each output sums the same products in the same order), and
+    sampled outputs are within the oracle's tolerance."""
+    M, K = 256, 3584
+    x = synth.activations(synth.rng(33, role=1), M, K)
+    xd = to_dev_f16(x)
+    for members in (("q", 3584), ("k", 512), ("v", 512)), (("gate", 18944), ("up", 18944)):
+        qs = [synth.weights(synth.Q4_K, synth.rng(33, 0, i, n), n, K) for i, (_, n) in enumerate(members)]
+        grouped = np.concatenate([q.reshape(n, -1) for q, (_, n) in zip(qs, members)])
+        n_tot = grouped.shape[0]
+        announce("gemm_fused grouped", "+".join(m for m, _ in members), f"M={M} N={n_tot} K={K}")
+        yg = to_host(mq.gemm_fused(xd, to_dev_u8(grouped), synth.Q4_K, n_tot, K, split_k=1))
+        c0 = 0
+        for q, (name, n) in zip(qs, members):
+            y = to_host(mq.gemm_fused(xd, to_dev_u8(q), synth.Q4_K, n, K, split_k=1))
+            assert np.array_equal(yg[:, c0:c0 + n], y), f"{name}: grouped != per-matrix"
+            c0 += n
+        rows = np.array([0, 77, 255])
+        cols = np.unique(np.concatenate([[0, n_tot - 1], np.random.default_rng(n_tot).choice(n_tot, 62)]))
+        w = oracle.dequant_ref(synth.Q4_K, grouped[cols].reshape(-1), len(cols), K)
+        check_gemm(yg[rows][:, cols], x, w, K, "grouped fused", rows=rows)
