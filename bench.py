@@ -91,6 +91,9 @@ def parse():
                    help="profiling aid: run only this 7B matrix's fused GEMM --steps times")
     p.add_argument("--only-mmq", default=None,
                    help="time only this 7B shape on the int8 path (for counter runs)")
+    p.add_argument("--only-small-m", action="store_true",
+                   help="profiling aid: M = 128 Q4_K GEMMs (cache and fused) on 4096x4096 with "
+                        "K splits 0, 1, 2, 4, 8, 16 and on 14336x4096, 30 calls each")
     p.add_argument("--only-sweep", action="store_true",
                    help="only the fused-vs-cache sweep (for a kernel trace of its calls); "
                         "prints its JSON")
@@ -204,6 +207,30 @@ def run_only_mmq(torch, mq, name, steps, dev):
     print(json.dumps({"only_mmq": name, "M": M, "N": N, "K": K, "calls": steps + 1,
                       "median_call_us": round(us, 2),
                       "tops": round(2.0 * M * N * K / us / 1e6, 1)}), flush=True)
+
+
+def run_only_small_m(torch, mq, dev):
+    """M = 128 GEMMs for counter runs: per (shape, path, split) 30 calls in a
+    fixed order, so the dispatches of a trace can be attributed in order."""
+    M, fmt = 128, synth.Q4_K
+    order = []
+    for N, K in ((4096, 4096), (14336, 4096)):
+        q = synth.weights_device(fmt, 1, N, K, dev)
+        c = mq.dequant_to_f16(q, fmt, N, K)
+        x = synth.activations_device(2, M, K, dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        for path in ("fused", "cache"):
+            for split in ((0, 1, 2, 4, 8, 16) if N == 4096 else (0,)):
+                wsb = mq.workspace_bytes(fmt if path == "fused" else 0, M, N, K, split)
+                ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
+                for _ in range(30):
+                    if path == "fused":
+                        mq.gemm_fused(x, q, fmt, N, K, split_k=split, out=y, ws=ws)
+                    else:
+                        mq.gemm_f16cache(x, c, K, split_k=split, out=y, ws=ws)
+                torch.cuda.synchronize()
+                order.append(f"{path} {N}x{K} split {split}")
+    print(json.dumps({"only_small_m": order, "calls_each": 30}), flush=True)
 
 
 def run_calib_copy(torch, steps, dev):
@@ -930,6 +957,9 @@ def main():
         return
     if args.only_mmq:
         run_only_mmq(torch, mq, args.only_mmq, args.steps, dev)
+        return
+    if args.only_small_m:
+        run_only_small_m(torch, mq, dev)
         return
     if args.only_sweep:
         rows = []
