@@ -432,6 +432,17 @@ def _median_us(torch, fn, reps, warm=2):
     return graph_us(torch, [lambda r=r: fn(r) for r in range(reps)])
 
 
+def hbm_fill_gbs(torch, dev, nbytes=4 << 30, reps=5):
+    """A plain device fill of `nbytes` (torch zero_): the write-only rate,
+    beside the copy, for a pass like the decode whose bytes are three
+    quarters writes."""
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    us = graph_us(torch, [lambda: dst.zero_() for _ in range(reps)])
+    del dst
+    torch.cuda.empty_cache()
+    return nbytes / us / 1e3
+
+
 def hbm_copy_gbs(torch, dev, nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of `nbytes` (torch copy_), GB/s counting
     the bytes read plus the bytes written: the practical HBM ceiling the
@@ -990,7 +1001,9 @@ def main():
     log(f"[bench] {layers * 7} weights drawn on device in {time.time() - t0:.1f}s: "
         f"{qbytes / 1e9:.3f} GB quantized, {cbytes / 1e9:.3f} GB f16")
     copy_gbs = hbm_copy_gbs(torch, dev)
-    log(f"[bench] plain device copy (1 GiB, read + write): {copy_gbs:.0f} GB/s")
+    fill_gbs = hbm_fill_gbs(torch, dev)
+    log(f"[bench] plain device copy (1 GiB, read + write): {copy_gbs:.0f} GB/s; "
+        f"fill (4 GiB, write only): {fill_gbs:.0f} GB/s")
     deq_ms, rec = load_phase(torch, mq, W, args.load_reps)
     deq_gbs = (qbytes + cbytes) / (deq_ms / 1e3) / 1e9
     per_fmt = {}
@@ -1242,6 +1255,7 @@ def main():
             "frac": round(deq_gbs / PEAK_HBM_GBS, 4),
             "hbm_copy_gbs": round(copy_gbs, 1),
             "frac_of_copy": round(deq_gbs / copy_gbs, 4),
+            "hbm_fill_gbs": round(fill_gbs, 1),
         },
         "forward_check": fwd_check,
         "fused": fused,
