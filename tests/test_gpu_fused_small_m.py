@@ -59,3 +59,25 @@ def test_small_m_integer_exact_with_splits(fmt, split):
     rows = np.array([0, 1, 31, 32, 63, 64, 98, 99])
     Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(fmt, q, N, K))
     assert np.array_equal(Y[rows].astype(np.float64), Yref)
+
+
+@pytest.mark.parametrize("M,N", [(37, 1000), (100, 1000), (300, 5000)])
+@pytest.mark.parametrize("fmt", [12, 13])
+def test_k_ranges_start_at_every_superblock_position(fmt, M, N):
+    """The 128-column Q4_K / Q5_K tiles (64, 128 and 256 rows) with a forced
+    split of 56 k-steps into ranges of 7: ranges start at every residue mod 4
+    (0, 7, 14, 21, ...), so a range begins and ends inside a super-block and
+    its first step decodes a quarter other than the first; the last block of a
+    row is followed by the next row's bytes or the end of the matrix, and N is
+    ragged.  Integer inputs: every sampled element exact."""
+    K = 3584
+    p = mq.gemm_plan(fmt, M, N, K, 9)
+    assert p["bn"] == 128 and p["steps_per_split"] == 7 and p["split"] == 8
+    q = synth.weights(fmt, synth.rng(72, M, fmt, N), N, K, mode="integer")
+    x = synth.activations(synth.rng(72, M, role=1), M, K, mode="integer")
+    announce("K ranges in super-blocks", FMT_NAME[fmt], f"M={M}", f"N={N}", f"K={K}", "split=9",
+             f"tile={p['bm']}x{p['bn']}")
+    Y = to_host(mq.gemm_fused(to_dev_f16(x), to_dev_u8(q), fmt, N, K, split_k=9))
+    rows = np.unique(np.array([0, 1, 31, 36, M // 2, M - 1]))
+    Yref, _ = oracle.gemm_ref(x[rows], oracle.dequant_ref(fmt, q, N, K))
+    assert np.array_equal(Y[rows].astype(np.float64), Yref)
