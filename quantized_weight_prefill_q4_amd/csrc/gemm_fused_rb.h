@@ -162,38 +162,56 @@ __device__ __forceinline__ void rb_fetch(const u32x4 *Bc, int lane, int wave, Rb
 // One k-step of the wave's 256 × 64 tile from X stage Ac and the raw bytes
 // `cur` (fetched during the previous step); fetches the next step's raw
 // bytes (quarter NC4 of buffer Bnext) into `nxt` between the MFMAs.
+// The register-expansion steps prepare the operands of k-slice kk + 1 while
+// slice kk's 2·FM MFMAs run: A fragment i is read after MFMA i and the two
+// expanded B fragments are made after MFMAs FM and FM + 2, so that the wave —
+// alone on its SIMD — keeps feeding the matrix pipe instead of stopping for
+// one burst of LDS reads and expansion arithmetic (3-5% on the 7B gate|up,
+// down and 14336 x 4096 shapes at M = 2048).  Called after MFMA IJ of slice
+// kk; load_a(i) reads A fragment i of slice kk + 1, make_b(f) expands B
+// fragment f.
+// A fragment i (activation rows 32i .. 32i + 31) of k-slice kk from an X stage
+// (all the tile's rows, as every wave of these kernels reads).
+__device__ __forceinline__ half8 rb_a_frag(const u32x4 *Ac, int kk, int i, int lane) {
+    const int r = i * 32 + (lane & 31), c = kk * 2 + (lane >> 5);
+    return __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
+}
+
+template <int FM, int IJ, class LoadA, class MakeB>
+__device__ __forceinline__ void rb_next_operands(LoadA &&load_a, MakeB &&make_b) {
+    static_assert(FM >= 4, "a slice needs FM + 3 MFMAs to place the operands");
+    if constexpr (IJ < FM) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(std::integral_constant<int, IJ>());
+        __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (IJ == FM || IJ == FM + 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        make_b(std::integral_constant<int, (IJ - FM) / 2>());
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int FMT, int NC4, int FM, class Slot>
 __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32x16 (&acc)[FM][2],
                                         int lane, int wave, const RbRaw &cur, RbRaw &nxt,
                                         Slot &&slot) {
-    const int h = lane >> 5;
     half8 af[2][FM], bf[2][2];
-    auto load_a = [&](auto KKc, half8(&dst)[FM]) MQ_INLINE {
-        constexpr int kk = KKc;
-        const int c = kk * 2 + h;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int r = i * 32 + (lane & 31);
-            dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
-        }
-    };
-    load_a(std::integral_constant<int, 0>(), af[0]);
+    for (int i = 0; i < FM; ++i) af[0][i] = rb_a_frag(Ac, 0, i, lane);
     bf[0][0] = cur.bf0[0];
     bf[0][1] = cur.bf0[1];
     static_for<4>([&](auto KK) MQ_INLINE {
         constexpr int kk = KK, c = kk & 1;
-        if constexpr (kk + 1 < 4) {
-            load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
-#pragma unroll
-            for (int f = 0; f < 2; ++f) bf[c ^ 1][f] = q4k_frag<FMT, kk + 1>(cur, f);
-        } else {
-            rb_fetch<FMT, NC4>(Bnext, lane, wave, nxt);
-        }
+        if constexpr (kk + 1 == 4) rb_fetch<FMT, NC4>(Bnext, lane, wave, nxt);
         __builtin_amdgcn_sched_barrier(0);
         static_for<2 * FM>([&](auto IJ) MQ_INLINE {
             constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
             acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
                                                                0);
+            if constexpr (kk + 1 < 4)
+                rb_next_operands<FM, IJ>(
+                    [&](auto I) MQ_INLINE { af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane); },
+                    [&](auto F) MQ_INLINE { bf[c ^ 1][F] = q4k_frag<FMT, kk + 1>(cur, F); });
             if constexpr (n & 1) {
                 __builtin_amdgcn_sched_barrier(0);
                 slot(std::integral_constant<int, n / 2>());
@@ -417,34 +435,24 @@ __device__ __forceinline__ half8 q6k_frag(const R6Raw &r, int f) {
 template <int C2, int FM, class Slot>
 __device__ __forceinline__ void rb6_step(const u32x4 *Ac, const u32x4 *Bc, int h,
                                          f32x16 (&acc)[FM][2], int lane, int wave, Slot &&slot) {
-    const int hl = lane >> 5;
     R6Raw raw;
     r6_fetch<C2>(Bc, h, lane, wave, raw);
     half8 af[2][FM], bf[2][2];
-    auto load_a = [&](auto KKc, half8(&dst)[FM]) MQ_INLINE {
-        constexpr int kk = KKc;
-        const int c = kk * 2 + hl;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int r = i * 32 + (lane & 31);
-            dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
-        }
-    };
-    load_a(std::integral_constant<int, 0>(), af[0]);
+    for (int i = 0; i < FM; ++i) af[0][i] = rb_a_frag(Ac, 0, i, lane);
     bf[0][0] = q6k_frag<C2, 0>(raw, 0);
     bf[0][1] = q6k_frag<C2, 0>(raw, 1);
     static_for<4>([&](auto KK) MQ_INLINE {
         constexpr int kk = KK, c = kk & 1;
-        if constexpr (kk + 1 < 4) {
-            load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
-            bf[c ^ 1][0] = q6k_frag<C2, kk + 1>(raw, 0);
-            bf[c ^ 1][1] = q6k_frag<C2, kk + 1>(raw, 1);
-        }
         __builtin_amdgcn_sched_barrier(0);
         static_for<2 * FM>([&](auto IJ) MQ_INLINE {
             constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
             acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
                                                                0);
+            if constexpr (kk + 1 < 4)
+                rb_next_operands<FM, IJ>(
+                    [&](auto I) MQ_INLINE { af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane); },
+                    [&](auto F) MQ_INLINE { bf[c ^ 1][F] = q6k_frag<C2, kk + 1>(raw, F); });
             if constexpr (n & 1) {
                 __builtin_amdgcn_sched_barrier(0);
                 slot(std::integral_constant<int, n / 2>());
@@ -727,34 +735,24 @@ __device__ __forceinline__ half8 b32_frag(const B32Raw &r, int f) {
 template <int FMT, int C2, int FM, class Slot>
 __device__ __forceinline__ void b32_step(const u32x4 *Ac, const u32x4 *Bc, int o4,
                                          f32x16 (&acc)[FM][2], int lane, int wave, Slot &&slot) {
-    const int hl = lane >> 5;
     B32Raw raw;
     b32_fetch<FMT, C2>(Bc, o4, lane, wave, raw);
     half8 af[2][FM], bf[2][2];
-    auto load_a = [&](auto KKc, half8(&dst)[FM]) MQ_INLINE {
-        constexpr int kk = KKc;
-        const int c = kk * 2 + hl;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int r = i * 32 + (lane & 31);
-            dst[i] = __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
-        }
-    };
-    load_a(std::integral_constant<int, 0>(), af[0]);
+    for (int i = 0; i < FM; ++i) af[0][i] = rb_a_frag(Ac, 0, i, lane);
     bf[0][0] = b32_frag<FMT, 0>(raw, 0);
     bf[0][1] = b32_frag<FMT, 0>(raw, 1);
     static_for<4>([&](auto KK) MQ_INLINE {
         constexpr int kk = KK, c = kk & 1;
-        if constexpr (kk + 1 < 4) {
-            load_a(std::integral_constant<int, kk + 1>(), af[c ^ 1]);
-            bf[c ^ 1][0] = b32_frag<FMT, kk + 1>(raw, 0);
-            bf[c ^ 1][1] = b32_frag<FMT, kk + 1>(raw, 1);
-        }
         __builtin_amdgcn_sched_barrier(0);
         static_for<2 * FM>([&](auto IJ) MQ_INLINE {
             constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
             acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
                                                                0);
+            if constexpr (kk + 1 < 4)
+                rb_next_operands<FM, IJ>(
+                    [&](auto I) MQ_INLINE { af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane); },
+                    [&](auto F) MQ_INLINE { bf[c ^ 1][F] = b32_frag<FMT, kk + 1>(raw, F); });
             if constexpr (n & 1) {
                 __builtin_amdgcn_sched_barrier(0);
                 slot(std::integral_constant<int, n / 2>());

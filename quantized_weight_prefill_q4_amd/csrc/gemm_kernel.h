@@ -708,27 +708,59 @@ __device__ __forceinline__ void load_frags(const u32x4 *Ac, const u32x4 *Bc, int
     }
 }
 
+// One MFMA operand fragment (A when IDX < FM, else B fragment IDX − FM) of
+// k-slice kk.
+template <int FM, int FN, int TM, int TN, int IDX>
+__device__ __forceinline__ half8 load_frag(const u32x4 *Ac, const u32x4 *Bc, int kk, int wm, int wn,
+                                           int lane) {
+    const int c = kk * 2 + (lane >> 5);
+    if constexpr (IDX < FM) {
+        const int r = wm * TM + IDX * 32 + (lane & 31);
+        return __builtin_bit_cast(half8, Ac[r * 8 + (c ^ swz<8>(r))]);
+    } else {
+        const int r = wn * TN + (IDX - FM) * 32 + (lane & 31);
+        return __builtin_bit_cast(half8, Bc[r * 8 + (c ^ swz<8>(r))]);
+    }
+}
+
 // One 64-wide k-step of MFMAs from LDS stage (Ac, Bc) into the wave's tile,
 // with the loaders' work for other steps threaded through it: after every
 // second MFMA, slot(integral_constant<s>) runs, s = 0 .. FM·FN·2 − 1.
 // Fragments are double-buffered: the LDS reads of k-slice kk+1 are issued
-// before the MFMAs of slice kk.  Scheduling barriers fix the order, so loads
-// and LDS writes are issued between matrix instructions instead of in one
-// burst.
-template <int FM, int FN, int TM, int TN, class Slot>
+// before the MFMAs of slice kk, or with SPREAD_REQ one after each of slice
+// kk's first FM + FN MFMAs, so that a wave with one SIMD to itself never
+// stops feeding the matrix pipe for a burst of reads.  Scheduling barriers fix
+// the order, so loads and LDS writes are issued between matrix instructions
+// instead of in one burst.
+template <int FM, int FN, int TM, int TN, bool SPREAD_REQ = false, class Slot>
 __device__ __forceinline__ void mma_step(const u32x4 *Ac, const u32x4 *Bc, f32x16 (&acc)[FM][FN],
                                          int wm, int wn, int lane, Slot &&slot) {
+    // spreading needs a slice with at least as many MFMAs as fragments
+    constexpr bool SPREAD = SPREAD_REQ && FM * FN >= FM + FN;
     half8 af[2][FM], bf[2][FN];
     load_frags<FM, FN, TM, TN>(Ac, Bc, 0, wm, wn, lane, af[0], bf[0]);
     static_for<4>([&](auto KK) MQ_INLINE {
         constexpr int kk = KK, cur = kk & 1;
-        if constexpr (kk + 1 < 4)
+        if constexpr (!SPREAD && kk + 1 < 4)
             load_frags<FM, FN, TM, TN>(Ac, Bc, kk + 1, wm, wn, lane, af[cur ^ 1], bf[cur ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
         static_for<FM * FN>([&](auto IJ) MQ_INLINE {
             constexpr int i = IJ / FN, j = IJ % FN, n = (kk * FM + i) * FN + j;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], bf[cur][j], acc[i][j], 0,
                                                                0, 0);
+            // SPREAD: the next slice's fragments one after each of this slice's
+            // first FM + FN MFMAs, in the order the next slice first uses them
+            // (A0, B0 .. B(FN−1), A1 .. A(FM−1)), instead of in one burst
+            if constexpr (SPREAD && kk + 1 < 4 && IJ < FM + FN) {
+                constexpr int idx = IJ == 0 ? 0 : (IJ <= FN ? FM + IJ - 1 : IJ - FN);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (idx < FM)
+                    af[cur ^ 1][idx] = load_frag<FM, FN, TM, TN, idx>(Ac, Bc, kk + 1, wm, wn, lane);
+                else
+                    bf[cur ^ 1][idx - FM] =
+                        load_frag<FM, FN, TM, TN, idx>(Ac, Bc, kk + 1, wm, wn, lane);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if constexpr (n & 1) {
                 __builtin_amdgcn_sched_barrier(0);
                 slot(std::integral_constant<int, n / 2>());
@@ -948,7 +980,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         const bool live2 = kt + 2 < kt_end;
         la.begin(P, (kt + 2) * BK, live2);
         lb.begin(P, (kt + 2) * BK, live2 && bw);
-        mma_step<FM, FN, TM, TN>(P ? A1 : A0, P ? B1 : B0, acc, wm, wn, lane, [&](auto SL) MQ_INLINE {
+        // the 256 x 256 f16 tile spreads its fragment reads (2.6% on the 7B
+        // gate|up and down calls); on the 128-column tiles it measured no gain
+        // and 3% slower on the 7B o projection
+        constexpr bool SPREAD = BM == 256 && BN == 256 && FMT == kFmtF16;
+        mma_step<FM, FN, TM, TN, SPREAD>(P ? A1 : A0, P ? B1 : B0, acc, wm, wn, lane, [&](auto SL) MQ_INLINE {
             constexpr int sl = SL, half = sl < H ? sl : sl - H;
             constexpr int lo = half * (NA + NB) / H, hi = (half + 1) * (NA + NB) / H;
             static_for<hi - lo>([&](auto O) MQ_INLINE {
