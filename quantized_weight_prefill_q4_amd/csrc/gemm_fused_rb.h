@@ -133,35 +133,35 @@ __device__ __forceinline__ half8 q4k_frag(const RbRaw &r, int f) {
                                                KK < 2 ? r.C0[f] : r.C1[f]));
 }
 
+// The raw bytes of weight row part f (rows 64·wave + 32f + lane % 32) for
+// quarter C4 of the super-block: its 16-byte head and the lane's quant (and,
+// for Q5_K, fifth-bit) bytes.
 template <int FMT, int C4>
-__device__ __forceinline__ void rb_fetch(const u32x4 *Bc, int lane, int wave, RbRaw &r) {
+__device__ __forceinline__ void rb_fetch_row(const u32x4 *Bc, int lane, int wave, int f, RbRaw &r,
+                                             u32x4 &hdr) {
     using G = KRb<FMT>;
     const int h = lane >> 5;
-    u32x4 hdr[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * G::CH;   // the row's block
-        hdr[f] = blk[0];
-        const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk + G::QSC + 2 * C4);
-        r.qa[f] = q2[h];
-        r.qb[f] = q2[2 + h];
-        if constexpr (FMT == kFmtQ5_K) {
-            const u32x2 *h2 = reinterpret_cast<const u32x2 *>(blk + 1);
-            const u32x2 ha = h2[h], hb = h2[2 + h];
-            r.ha[f] = u32x2{ha.x >> (2 * C4), ha.y >> (2 * C4)};
-            r.hb[f] = u32x2{hb.x >> (2 * C4), hb.y >> (2 * C4)};
-        }
-    }
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        q4k_sub_scales<C4>(hdr[f], r.A0[f], r.C0[f], r.A1[f], r.C1[f]);
-        r.bf0[f] = q4k_frag<FMT, 0>(r, f);
+    const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * G::CH;   // the row's block
+    hdr = blk[0];
+    const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk + G::QSC + 2 * C4);
+    r.qa[f] = q2[h];
+    r.qb[f] = q2[2 + h];
+    if constexpr (FMT == kFmtQ5_K) {
+        const u32x2 *h2 = reinterpret_cast<const u32x2 *>(blk + 1);
+        const u32x2 ha = h2[h], hb = h2[2 + h];
+        r.ha[f] = u32x2{ha.x >> (2 * C4), ha.y >> (2 * C4)};
+        r.hb[f] = u32x2{hb.x >> (2 * C4), hb.y >> (2 * C4)};
     }
 }
 
-// One k-step of the wave's 256 × 64 tile from X stage Ac and the raw bytes
-// `cur` (fetched during the previous step); fetches the next step's raw
-// bytes (quarter NC4 of buffer Bnext) into `nxt` between the MFMAs.
+// Row part f's sub-block scales and mins from its head, and its first
+// k-slice's B fragment.
+template <int FMT, int C4>
+__device__ __forceinline__ void rb_fetch_finish(int f, const u32x4 &hdr, RbRaw &r) {
+    q4k_sub_scales<C4>(hdr, r.A0[f], r.C0[f], r.A1[f], r.C1[f]);
+    r.bf0[f] = q4k_frag<FMT, 0>(r, f);
+}
+
 // The register-expansion steps prepare the operands of k-slice kk + 1 while
 // slice kk's 2·FM MFMAs run: A fragment i is read after MFMA i and the two
 // expanded B fragments are made after MFMAs FM and FM + 2, so that the wave —
@@ -191,6 +191,9 @@ __device__ __forceinline__ void rb_next_operands(LoadA &&load_a, MakeB &&make_b)
     }
 }
 
+// One k-step of the wave's 256 × 64 tile from X stage Ac and the raw bytes
+// `cur` (fetched during the previous step); fetches the next step's raw
+// bytes (quarter NC4 of buffer Bnext) into `nxt` between the MFMAs.
 template <int FMT, int NC4, int FM, class Slot>
 __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32x16 (&acc)[FM][2],
                                         int lane, int wave, const RbRaw &cur, RbRaw &nxt,
@@ -200,18 +203,30 @@ __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32
     for (int i = 0; i < FM; ++i) af[0][i] = rb_a_frag(Ac, 0, i, lane);
     bf[0][0] = cur.bf0[0];
     bf[0][1] = cur.bf0[1];
+    u32x4 hdr[2];
     static_for<4>([&](auto KK) MQ_INLINE {
         constexpr int kk = KK, c = kk & 1;
-        if constexpr (kk + 1 == 4) rb_fetch<FMT, NC4>(Bnext, lane, wave, nxt);
         __builtin_amdgcn_sched_barrier(0);
         static_for<2 * FM>([&](auto IJ) MQ_INLINE {
             constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
             acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
                                                                0);
-            if constexpr (kk + 1 < 4)
+            if constexpr (kk + 1 < 4) {
                 rb_next_operands<FM, IJ>(
                     [&](auto I) MQ_INLINE { af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane); },
                     [&](auto F) MQ_INLINE { bf[c ^ 1][F] = q4k_frag<FMT, kk + 1>(cur, F); });
+            } else if constexpr (IJ == 0 || IJ == 2) {
+                // the last slice spreads the next step's raw fetch the same
+                // way: the row parts' reads after MFMAs 0 and 2, their scales
+                // and first fragments after MFMAs FM and FM + 2
+                __builtin_amdgcn_sched_barrier(0);
+                rb_fetch_row<FMT, NC4>(Bnext, lane, wave, IJ / 2, nxt, hdr[IJ / 2]);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (IJ == FM || IJ == FM + 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                rb_fetch_finish<FMT, NC4>((IJ - FM) / 2, hdr[(IJ - FM) / 2], nxt);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if constexpr (n & 1) {
                 __builtin_amdgcn_sched_barrier(0);
                 slot(std::integral_constant<int, n / 2>());
@@ -305,7 +320,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < NT; ++i) B[threadIdx.x + kThreads * i] = t[i];
         sync_lds();
-        rb_fetch<FMT, 0>(B, lane, wave, raw[0]);
+        for (int f = 0; f < 2; ++f) {
+            u32x4 hd;
+            rb_fetch_row<FMT, 0>(B, lane, wave, f, raw[0], hd);
+            rb_fetch_finish<FMT, 0>(f, hd, raw[0]);
+        }
     }
 
     // Step kt (quarter C4, P = C4 & 1): X as in gemm_kernel; raw weights:
@@ -403,15 +422,27 @@ struct R6Raw {
 };
 
 // h: the half of the super-block the step lies in; C2: its quarter in the half.
-template <int C2>
-__device__ __forceinline__ void r6_fetch(const u32x4 *Bc, int h, int lane, int wave, R6Raw &r) {
+// The low-bit bytes of k-slice KK for the lane's two weight rows.
+template <int KK>
+__device__ __forceinline__ void r6_fetch_ql(const u32x4 *Bc, int lane, int wave, R6Raw &r) {
     const int hl = lane >> 5;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * kR6Stride;
-        const u32x2 *q2 = reinterpret_cast<const u32x2 *>(blk);
+        const u32x2 *q2 =
+            reinterpret_cast<const u32x2 *>(Bc + (wave * 64 + f * 32 + (lane & 31)) * kR6Stride);
+        r.ql[f][KK] = q2[4 * (KK >> 1) + 2 * (KK & 1) + hl];
+    }
+}
+
+// Everything of the step but the low-bit bytes of k-slices 1-3 (read during
+// the slice before each, r6_fetch_ql).
+template <int C2>
+__device__ __forceinline__ void r6_fetch(const u32x4 *Bc, int h, int lane, int wave, R6Raw &r) {
+    const int hl = lane >> 5;
+    r6_fetch_ql<0>(Bc, lane, wave, r);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) r.ql[f][kk] = q2[4 * (kk >> 1) + 2 * (kk & 1) + hl];
+    for (int f = 0; f < 2; ++f) {
+        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * kR6Stride;
         const u32x2 *h2 = reinterpret_cast<const u32x2 *>(blk + 4);
         r.qh[f][0] = h2[hl];
         r.qh[f][1] = h2[2 + hl];
@@ -451,7 +482,11 @@ __device__ __forceinline__ void rb6_step(const u32x4 *Ac, const u32x4 *Bc, int h
                                                                0);
             if constexpr (kk + 1 < 4)
                 rb_next_operands<FM, IJ>(
-                    [&](auto I) MQ_INLINE { af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane); },
+                    [&](auto I) MQ_INLINE {
+                        af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane);
+                        // the next slice's low-bit bytes, FM MFMAs before use
+                        if constexpr (I == 0) r6_fetch_ql<kk + 1>(Bc, lane, wave, raw);
+                    },
                     [&](auto F) MQ_INLINE { bf[c ^ 1][F] = q6k_frag<C2, kk + 1>(raw, F); });
             if constexpr (n & 1) {
                 __builtin_amdgcn_sched_barrier(0);
