@@ -236,6 +236,65 @@ __device__ __forceinline__ void rb_step(const u32x4 *Ac, const u32x4 *Bnext, f32
     });
 }
 
+// rb_step with the step's barrier inside: af[0] holds k-slice 0's A
+// fragments on entry; mid() — the barrier — runs between slices 2 and 3, and
+// slice 3 reads, around the next step's raw fetch, the next step's slice-0 A
+// fragments from X stage An into af[0], so the next step starts on operands
+// already in registers.
+template <int FMT, int NC4, int FM, class Slot, class Mid>
+__device__ __forceinline__ void rb_step_x(const u32x4 *Ac, const u32x4 *An, const u32x4 *Bnext,
+                                          f32x16 (&acc)[FM][2], half8 (&af)[2][FM], int lane,
+                                          int wave, const RbRaw &cur, RbRaw &nxt, Slot &&slot,
+                                          Mid &&mid) {
+    static_assert(FM >= 4, "a slice needs FM + 3 MFMAs to place the operands");
+    half8 bf[2][2];
+    bf[0][0] = cur.bf0[0];
+    bf[0][1] = cur.bf0[1];
+    u32x4 hdr[2];
+    static_for<4>([&](auto KK) MQ_INLINE {
+        constexpr int kk = KK, c = kk & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<2 * FM>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
+                                                               0);
+            if constexpr (kk + 1 < 4) {
+                rb_next_operands<FM, IJ>(
+                    [&](auto I) MQ_INLINE { af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane); },
+                    [&](auto F) MQ_INLINE { bf[c ^ 1][F] = q4k_frag<FMT, kk + 1>(cur, F); });
+            } else if constexpr (IJ == 0 || IJ == 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                rb_fetch_row<FMT, NC4>(Bnext, lane, wave, IJ / 2, nxt, hdr[IJ / 2]);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (IJ == FM || IJ == FM + 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                rb_fetch_finish<FMT, NC4>((IJ - FM) / 2, hdr[(IJ - FM) / 2], nxt);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // the other positions of the last slice, in order, read the
+                // next step's slice-0 A fragments
+                constexpr int skip = (IJ > 0) + (IJ > 2) + (IJ > FM) + (IJ > FM + 2);
+                constexpr int ia = IJ - skip;
+                if constexpr (ia < FM) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    af[0][ia] = rb_a_frag(An, 0, ia, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (n & 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                slot(std::integral_constant<int, n / 2>());
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+        if constexpr (kk == 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            mid();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    });
+}
+
 template <int FMT, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
     static_assert(FMT == kFmtQ4_K || FMT == kFmtQ5_K, "Q4_K or Q5_K");
@@ -288,6 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
     }
     u32x4 bv[2][G::PER];
     RbRaw raw[2];   // raw bytes of the current and the next k-step (index P, 1 − P)
+    half8 af[2][FM];   // A fragments, k-slice 0 of a step read during the previous one
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -325,12 +385,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
             rb_fetch_row<FMT, 0>(B, lane, wave, f, raw[0], hd);
             rb_fetch_finish<FMT, 0>(f, hd, raw[0]);
         }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[0][i] = rb_a_frag(A0, 0, i, lane);
     }
 
     // Step kt (quarter C4, P = C4 & 1): X as in gemm_kernel; raw weights:
     // slots 0..15 load part (C4 + 1) & 3 of the super-block that step kt + 1
-    // writes into set P, slots 16..31 write set 1 − P (part C4 of super-block
-    // kt / 4 + 1) to that super-block's buffer.
+    // writes into set P, slots 8..23 (k-slices 1 and 2) write set 1 − P (part
+    // C4 of super-block kt / 4 + 1) to that super-block's buffer; the step's
+    // barrier follows slice 2 (rb_step_x).
     auto step = [&](auto C4c, int kt) MQ_INLINE {
         constexpr int C4 = decltype(C4c)::value, P = C4 & 1;
         constexpr int LC = (C4 + 1) & 3;
@@ -349,24 +412,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4k_rb_kernel(Args a) {
         const int sbl = (kt + 1) / 4 + 1;
         const uint32_t boff = sbl < sb_end ? (uint32_t)sbl * (uint32_t)G::BB : kOOB;
         la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
-        rb_step<FMT, (C4 + 1) & 3>(P ? A1 : A0, Bnext, acc, lane, wave, raw[P], raw[1 - P],
-                              [&](auto SL) MQ_INLINE {
-            constexpr int sl = SL, half = sl < H ? sl : sl - H;
-            constexpr int TOT = sl < H ? NA + NL : NA + NS;
-            constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
-            static_for<hi - lo>([&](auto O) MQ_INLINE {
-                constexpr int o = lo + O;
-                if constexpr (sl < H) {
+        rb_step_x<FMT, (C4 + 1) & 3>(P ? A1 : A0, An, Bnext, acc, af, lane, wave, raw[P],
+                                     raw[1 - P], [&](auto SL) MQ_INLINE {
+            constexpr int sl = SL;
+            if constexpr (sl < H) {
+                constexpr int lo = sl * (NA + NL) / H, hi = (sl + 1) * (NA + NL) / H;
+                static_for<hi - lo>([&](auto O) MQ_INLINE {
+                    constexpr int o = lo + O;
                     if constexpr (o < NA) la.load(P, o);
                     else bv[P][o - NA] = buf_load16(
                         rsb, boff == kOOB ? kOOB : goff[RbPart<FMT, LC>::lo + o - NA] + boff);
-                } else {
+                });
+            }
+            if constexpr (sl >= H / 2 && sl < H / 2 + H) {
+                constexpr int w = sl - H / 2;
+                constexpr int lo = w * (NA + NS) / H, hi = (w + 1) * (NA + NS) / H;
+                static_for<hi - lo>([&](auto O) MQ_INLINE {
+                    constexpr int o = lo + O;
                     if constexpr (o < NA) la.store(1 - P, o, An);
                     else Bn[threadIdx.x + kThreads * (RbPart<FMT, C4>::lo + o - NA)] = bv[1 - P][o - NA];
-                }
-            });
-        });
-        sync_lds();
+                });
+            }
+        }, [&]() MQ_INLINE { sync_lds(); });
     };
     for (int kt = kt_begin; kt < kt_end; kt += 4) {
         step(std::integral_constant<int, 0>(), kt);
