@@ -564,6 +564,102 @@ __device__ __forceinline__ void rb6_step(const u32x4 *Ac, const u32x4 *Bc, int h
     });
 }
 
+// r6_fetch in two parts, for placing between MFMAs: the LDS reads (the
+// factors' scale word and d in sw, db), then the factors d·s.
+template <int C2>
+__device__ __forceinline__ void r6_fetch_rows(const u32x4 *Bc, int h, int lane, int wave, R6Raw &r,
+                                              uint32_t (&sw)[2], uint32_t (&db)[2]) {
+    const int hl = lane >> 5;
+    r6_fetch_ql<0>(Bc, lane, wave, r);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const u32x4 *blk = Bc + (wave * 64 + f * 32 + (lane & 31)) * kR6Stride;
+        const u32x2 *h2 = reinterpret_cast<const u32x2 *>(blk + 4);
+        r.qh[f][0] = h2[hl];
+        r.qh[f][1] = h2[2 + hl];
+        sw[f] = reinterpret_cast<const uint32_t *>(blk + 6)[2 * h + C2];
+        db[f] = reinterpret_cast<const uint32_t *>(blk + 7)[3] >> 16;
+    }
+}
+__device__ __forceinline__ void r6_fetch_factors(R6Raw &r, const uint32_t (&sw)[2],
+                                                 const uint32_t (&db)[2]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const float d = f16_bits_to_f32(db[f]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) r.ds[f][kk] = d * (float)(int)(int8_t)(sw[f] >> (8 * kk));
+    }
+}
+
+// rb6_step with the step's barrier inside: on entry raw holds the step's
+// bytes (low-bit bytes of k-slice 0 only), af[0] its slice-0 A fragments and
+// bf0 its slice-0 B fragments; mid() — the barrier — runs between slices 2
+// and 3, and slice 3 prepares the next step (quarter C2N, half hn, raw bytes
+// in Bnx, X stage An) in raw, af[0] and bf0, so that it starts on operands
+// already in registers.
+template <int C2, int C2N, int FM, class Slot, class Mid>
+__device__ __forceinline__ void rb6_step_x(const u32x4 *Ac, const u32x4 *Bc, const u32x4 *An,
+                                           const u32x4 *Bnx, int hn, f32x16 (&acc)[FM][2],
+                                           R6Raw &raw, half8 (&af)[2][FM], half8 (&bf0)[2],
+                                           int lane, int wave, Slot &&slot, Mid &&mid) {
+    static_assert(FM >= 4, "a slice needs FM + 3 MFMAs to place the operands");
+    half8 bf[2][2];
+    bf[0][0] = bf0[0];
+    bf[0][1] = bf0[1];
+    uint32_t sw[2], db[2];
+    static_for<4>([&](auto KK) MQ_INLINE {
+        constexpr int kk = KK, c = kk & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<2 * FM>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
+                                                               0);
+            if constexpr (kk + 1 < 4) {
+                rb_next_operands<FM, IJ>(
+                    [&](auto I) MQ_INLINE {
+                        af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane);
+                        // the next slice's low-bit bytes, FM MFMAs before use
+                        if constexpr (I == 0) r6_fetch_ql<kk + 1>(Bc, lane, wave, raw);
+                    },
+                    [&](auto F) MQ_INLINE { bf[c ^ 1][F] = q6k_frag<C2, kk + 1>(raw, F); });
+            } else if constexpr (IJ == 0) {
+                // the last slice's operands are made: the next step's bytes
+                __builtin_amdgcn_sched_barrier(0);
+                r6_fetch_rows<C2N>(Bnx, hn, lane, wave, raw, sw, db);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (IJ == FM) {
+                __builtin_amdgcn_sched_barrier(0);
+                r6_fetch_factors(raw, sw, db);
+                bf0[0] = q6k_frag<C2N, 0>(raw, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (IJ == FM + 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                bf0[1] = q6k_frag<C2N, 0>(raw, 1);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // the other positions, in order: the next step's slice-0 A
+                constexpr int skip = (IJ > 0) + (IJ > FM) + (IJ > FM + 2);
+                constexpr int ia = IJ - skip;
+                if constexpr (ia < FM) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    af[0][ia] = rb_a_frag(An, 0, ia, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (n & 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                slot(std::integral_constant<int, n / 2>());
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+        if constexpr (kk == 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            mid();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    });
+}
+
 template <int FMT, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
     static_assert(FMT == kFmtQ6_K, "Q6_K only");
@@ -626,6 +722,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
         buf[(r0 + 32 * i) * kR6Stride + p] = realign16(bv[set][j], bsh[set][j]);
     };
 
+    // the step's operands, prepared during the previous step (rb6_step_x)
+    R6Raw raw;
+    half8 af[2][FM], bf0[2];
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -656,11 +755,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) bstore(0, i, 4 + i, B);
         sync_lds();
+        r6_fetch<0>(B, hx0 & 1, lane, wave, raw);   // kt_begin is even: quarter 0
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[0][i] = rb_a_frag(A0, 0, i, lane);
+        bf0[0] = q6k_frag<0, 0>(raw, 0);
+        bf0[1] = q6k_frag<0, 0>(raw, 1);
     }
 
     // Step kt (C2 = kt & 1 = P): slots 0..15 load part 1 − C2 of the half
     // that step kt + 1 writes (half kt/2 + 1 for C2 = 0, kt/2 + 2 for C2 = 1)
-    // into set P; slots 16..31 write set 1 − P (part C2 of half kt/2 + 1).
+    // into set P; slots 8..23 (k-slices 1 and 2) write set 1 − P (part C2 of
+    // half kt/2 + 1); the step's barrier follows slice 2 (rb6_step_x), after
+    // which the next step's bytes are read: from this half's buffer after
+    // quarter 0, from the next half's (complete) after quarter 1.
     auto step = [&](auto C2c, int kt) MQ_INLINE {
         constexpr int C2 = decltype(C2c)::value, P = C2;
         constexpr int H = 2 * FM, NB = 4;   // H: half the step's slots
@@ -671,22 +778,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q6k_rb_kernel(Args a) {
         const int hl_next = C2 == 0 ? hx + 1 : hx + 2;
         constexpr int lpart = 1 - C2;
         la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
-        rb6_step<C2>(P ? A1 : A0, Bc, hx & 1, acc, lane, wave, [&](auto SL) MQ_INLINE {
-            constexpr int sl = SL, half = sl < H ? sl : sl - H;
-            constexpr int TOT = NA + NB;
-            constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
-            static_for<hi - lo>([&](auto O) MQ_INLINE {
-                constexpr int o = lo + O;
+        constexpr int TOT = NA + NB;
+        rb6_step_x<C2, 1 - C2>(
+            P ? A1 : A0, Bc, An, C2 == 0 ? Bc : Bn, C2 == 0 ? (hx & 1) : ((hx + 1) & 1), acc, raw,
+            af, bf0, lane, wave,
+            [&](auto SL) MQ_INLINE {
+                constexpr int sl = SL;
                 if constexpr (sl < H) {
-                    if constexpr (o < NA) la.load(P, o);
-                    else bload(P, o - NA, 4 * lpart + (o - NA), hl_next);
-                } else {
-                    if constexpr (o < NA) la.store(1 - P, o, An);
-                    else bstore(1 - P, o - NA, 4 * C2 + (o - NA), Bn);
+                    constexpr int lo = sl * TOT / H, hi = (sl + 1) * TOT / H;
+                    static_for<hi - lo>([&](auto O) MQ_INLINE {
+                        constexpr int o = lo + O;
+                        if constexpr (o < NA) la.load(P, o);
+                        else bload(P, o - NA, 4 * lpart + (o - NA), hl_next);
+                    });
                 }
-            });
-        });
-        sync_lds();
+                if constexpr (sl >= H / 2 && sl < H / 2 + H) {
+                    constexpr int w = sl - H / 2;
+                    constexpr int lo = w * TOT / H, hi = (w + 1) * TOT / H;
+                    static_for<hi - lo>([&](auto O) MQ_INLINE {
+                        constexpr int o = lo + O;
+                        if constexpr (o < NA) la.store(1 - P, o, An);
+                        else bstore(1 - P, o - NA, 4 * C2 + (o - NA), Bn);
+                    });
+                }
+            },
+            [&]() MQ_INLINE { sync_lds(); });
     };
     for (int kt = kt_begin; kt < kt_end; kt += 2) {
         step(std::integral_constant<int, 0>(), kt);
@@ -777,11 +893,11 @@ struct B32Raw {
 // o4: the staged row's first block at dword o4 (0, or 2 for odd halves of
 // Q8_0, Q4_0 and Q5_0).
 template <int FMT, int C2>
-__device__ __forceinline__ void b32_fetch(const u32x4 *Bc, int o4, int lane, int wave, B32Raw &r) {
+__device__ __forceinline__ void b32_fetch_row(const u32x4 *Bc, int o4, int lane, int wave, int f,
+                                              B32Raw &r) {
     using G = B32Rb<FMT>;
     const int hl = lane >> 5;
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    {
         const uint32_t *rw =
             reinterpret_cast<const uint32_t *>(Bc + (wave * 64 + f * 32 + (lane & 31)) * G::S) + o4;
         const uint32_t *rh = rw + 2 * hl;   // + 8 bytes for the upper half-wave
@@ -815,6 +931,11 @@ __device__ __forceinline__ void b32_fetch(const u32x4 *Bc, int o4, int lane, int
             else r.c[f][bb] = 0.0f;
         });
     }
+}
+template <int FMT, int C2>
+__device__ __forceinline__ void b32_fetch(const u32x4 *Bc, int o4, int lane, int wave, B32Raw &r) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) b32_fetch_row<FMT, C2>(Bc, o4, lane, wave, f, r);
 }
 
 template <int FMT, int KK>
@@ -861,6 +982,63 @@ __device__ __forceinline__ void b32_step(const u32x4 *Ac, const u32x4 *Bc, int o
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
+    });
+}
+
+// b32_step with the step's barrier inside (as rb6_step_x): raw, af[0] and
+// bf0 hold the step's bytes and slice-0 fragments on entry; slice 3, after
+// the barrier, prepares the next step's (quarter C2N, first block at dword
+// o4n of buffer Bnx, X stage An).
+template <int FMT, int C2, int C2N, int FM, class Slot, class Mid>
+__device__ __forceinline__ void b32_step_x(const u32x4 *Ac, const u32x4 *An, const u32x4 *Bnx,
+                                           int o4n, f32x16 (&acc)[FM][2], B32Raw &raw,
+                                           half8 (&af)[2][FM], half8 (&bf0)[2], int lane,
+                                           int wave, Slot &&slot, Mid &&mid) {
+    static_assert(FM >= 4, "a slice needs FM + 3 MFMAs to place the operands");
+    half8 bf[2][2];
+    bf[0][0] = bf0[0];
+    bf[0][1] = bf0[1];
+    static_for<4>([&](auto KK) MQ_INLINE {
+        constexpr int kk = KK, c = kk & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<2 * FM>([&](auto IJ) MQ_INLINE {
+            constexpr int i = IJ / 2, f = IJ % 2, n = kk * 2 * FM + IJ;
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][f], acc[i][f], 0, 0,
+                                                               0);
+            if constexpr (kk + 1 < 4) {
+                rb_next_operands<FM, IJ>(
+                    [&](auto I) MQ_INLINE { af[c ^ 1][I] = rb_a_frag(Ac, kk + 1, I, lane); },
+                    [&](auto F) MQ_INLINE { bf[c ^ 1][F] = b32_frag<FMT, kk + 1>(raw, F); });
+            } else if constexpr (IJ == 0 || IJ == 2) {
+                // the last slice's operands are made: the next step's bytes
+                __builtin_amdgcn_sched_barrier(0);
+                b32_fetch_row<FMT, C2N>(Bnx, o4n, lane, wave, IJ / 2, raw);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (IJ == FM || IJ == FM + 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                bf0[(IJ - FM) / 2] = b32_frag<FMT, 0>(raw, (IJ - FM) / 2);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // the other positions, in order: the next step's slice-0 A
+                constexpr int skip = (IJ > 0) + (IJ > 2) + (IJ > FM) + (IJ > FM + 2);
+                constexpr int ia = IJ - skip;
+                if constexpr (ia < FM) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    af[0][ia] = rb_a_frag(An, 0, ia, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (n & 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                slot(std::integral_constant<int, n / 2>());
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+        if constexpr (kk == 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            mid();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     });
 }
 
@@ -926,6 +1104,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
     };
     auto bstore = [&](int set, int j, int i, u32x4 *buf) MQ_INLINE { buf[lpos[i]] = bv[set][j]; };
 
+    // Q8_0 and Q5_0 run the step with its barrier inside (b32_step_x; Q4_0
+    // and Q5_1 would spill registers there and keep b32_step): the step's
+    // operands are then prepared during the previous step
+    constexpr bool XS = FMT == kFmtQ8_0 || FMT == kFmtQ5_0;
+    B32Raw raw;
+    half8 af[2][FM], bf0[2];
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -956,11 +1140,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < G::CH - G::P0; ++i) bstore(0, i, G::P0 + i, B);
         sync_lds();
+        if constexpr (XS) {
+            b32_fetch<FMT, 0>(B, OODD * (hx0 & 1), lane, wave, raw);   // kt_begin is even
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[0][i] = rb_a_frag(A0, 0, i, lane);
+            bf0[0] = b32_frag<FMT, 0>(raw, 0);
+            bf0[1] = b32_frag<FMT, 0>(raw, 1);
+        }
     }
 
     // Step kt (C2 = kt & 1 = P): slots 0..15 load part 1 − C2 of the half
     // that step kt + 1 writes (half kt/2 + 1 for C2 = 0, kt/2 + 2 for C2 = 1)
-    // into set P; slots 16..31 write set 1 − P (part C2 of half kt/2 + 1).
+    // into set P; slots 16..31 write set 1 − P (part C2 of half kt/2 + 1),
+    // or with XS slots 8..23 (k-slices 1 and 2), the step's barrier following
+    // slice 2, after which the next step's bytes are read: from this half's
+    // buffer after quarter 0, from the next half's (complete) after quarter 1.
     auto step = [&](auto C2c, int kt) MQ_INLINE {
         constexpr int C2 = decltype(C2c)::value, P = C2;
         constexpr int H = 2 * FM;   // half the step's slots
@@ -973,22 +1167,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_b32_rb_kernel(Args a) {
         u32x4 *Bn = (hx & 1) ? Bq0 : Bq1;
         const int hl_next = C2 == 0 ? hx + 1 : hx + 2;
         la.begin(P, (kt + 2) * BK, kt + 2 < kt_end);
-        b32_step<FMT, C2>(P ? A1 : A0, Bc, OODD * (hx & 1), acc, lane, wave, [&](auto SL) MQ_INLINE {
-            constexpr int sl = SL, half = sl < H ? sl : sl - H;
-            constexpr int TOT = NA + (sl < H ? NBL : NBS);
-            constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
-            static_for<hi - lo>([&](auto O) MQ_INLINE {
-                constexpr int o = lo + O;
-                if constexpr (sl < H) {
-                    if constexpr (o < NA) la.load(P, o);
-                    else bload(P, o - NA, B32Part<FMT, lpart>::lo + (o - NA), hl_next);
-                } else {
-                    if constexpr (o < NA) la.store(1 - P, o, An);
-                    else bstore(1 - P, o - NA, B32Part<FMT, C2>::lo + (o - NA), Bn);
-                }
+        if constexpr (!XS) {
+            b32_step<FMT, C2>(P ? A1 : A0, Bc, OODD * (hx & 1), acc, lane, wave, [&](auto SL) MQ_INLINE {
+                constexpr int sl = SL, half = sl < H ? sl : sl - H;
+                constexpr int TOT = NA + (sl < H ? NBL : NBS);
+                constexpr int lo = half * TOT / H, hi = (half + 1) * TOT / H;
+                static_for<hi - lo>([&](auto O) MQ_INLINE {
+                    constexpr int o = lo + O;
+                    if constexpr (sl < H) {
+                        if constexpr (o < NA) la.load(P, o);
+                        else bload(P, o - NA, B32Part<FMT, lpart>::lo + (o - NA), hl_next);
+                    } else {
+                        if constexpr (o < NA) la.store(1 - P, o, An);
+                        else bstore(1 - P, o - NA, B32Part<FMT, C2>::lo + (o - NA), Bn);
+                    }
+                });
             });
-        });
-        sync_lds();
+            sync_lds();
+            return;
+        }
+        const int hxn = C2 == 0 ? hx : hx + 1;
+        b32_step_x<FMT, C2, 1 - C2>(
+            P ? A1 : A0, An, C2 == 0 ? Bc : Bn, OODD * (hxn & 1), acc, raw, af, bf0, lane, wave,
+            [&](auto SL) MQ_INLINE {
+                constexpr int sl = SL;
+                if constexpr (sl < H) {
+                    constexpr int lo = sl * (NA + NBL) / H, hi = (sl + 1) * (NA + NBL) / H;
+                    static_for<hi - lo>([&](auto O) MQ_INLINE {
+                        constexpr int o = lo + O;
+                        if constexpr (o < NA) la.load(P, o);
+                        else bload(P, o - NA, B32Part<FMT, lpart>::lo + (o - NA), hl_next);
+                    });
+                }
+                if constexpr (sl >= H / 2 && sl < H / 2 + H) {
+                    constexpr int w = sl - H / 2;
+                    constexpr int lo = w * (NA + NBS) / H, hi = (w + 1) * (NA + NBS) / H;
+                    static_for<hi - lo>([&](auto O) MQ_INLINE {
+                        constexpr int o = lo + O;
+                        if constexpr (o < NA) la.store(1 - P, o, An);
+                        else bstore(1 - P, o - NA, B32Part<FMT, C2>::lo + (o - NA), Bn);
+                    });
+                }
+            },
+            [&]() MQ_INLINE { sync_lds(); });
     };
     for (int kt = kt_begin; kt < kt_end; kt += 2) {
         step(std::integral_constant<int, 0>(), kt);
