@@ -913,10 +913,10 @@ __device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN],
 // (j+1)%2 (second half).  The barrier at the end of the step publishes that
 // stage; it also orders the reads of stage j%2 before its refill at the end
 // of step j+1.  A global load thus has from its issue in step j until the
-// second half of step j+1 to arrive.  The 256 × 256 f16 tile moves the
-// barrier inside the step (mma_step_x): its LDS writes take k-slices 1 and
-// 2, the barrier follows, and slice 3 reads the next step's first
-// fragments from the stage just published (a load then has 1.25 steps).
+// second half of step j+1 to arrive.  The 256 × 256 and 256 × 128 f16-cache
+// tiles move the barrier inside the step (mma_step_x): their LDS writes take
+// k-slices 1 and 2, the barrier follows, and slice 3 reads the next step's
+// first fragments from the stage just published (a load then has 1.25 steps).
 // BM × BN: block tile, split over NWV waves.  NWV = 4 (2×2 waves): one wave
 // per SIMD, whose register file then holds a 128 × 128 sub-tile's 256
 // accumulators (the 256 × 256 tile) or the fused loaders' raw bytes.  NWV = 8
@@ -1017,10 +1017,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
             if (bw) lb.store(0, i, B0);
         sync_lds();
     }
-    // the 256 x 256 f16 tile runs the step with its barrier inside
-    // (mma_step_x; the 7B down call 3.7% faster, gate|up 0.5%): its fragment
-    // registers live across steps
-    constexpr bool XS = BM == 256 && BN == 256 && FMT == kFmtF16;
+    // the f16-cache tiles whose k-slices have at least as many MFMAs as
+    // fragments (256 x 256, 256 x 128) run the step with its barrier inside
+    // (mma_step_x; the 7B down call 3.7% faster, gate|up 0.5%, q|k|v and o
+    // 0.5%): their fragment registers live across steps
+    constexpr bool XS = FMT == kFmtF16 && !XF32 && FM * FN >= FM + FN;
     half8 xaf[2][FM], xbf[2][FN];
     if constexpr (XS) load_frags<FM, FN, TM, TN>(A0, B0, 0, wm, wn, lane, xaf[0], xbf[0]);
 
@@ -1036,22 +1037,29 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         la.begin(P, (kt + 2) * BK, live2);
         lb.begin(P, (kt + 2) * BK, live2 && bw);
         if constexpr (XS) {
-            // slots 0 .. NA+NB-1 issue the loads of step kt+2 into set P;
-            // slots 8 .. 8+NA+NB-1 (k-slices 1 and 2) write set 1-P to stage
-            // 1-P, published by the barrier before slice 3
-            static_assert(NA + NB == 16 && H == 16, "the 256 x 256 f16 slot plan");
+            // slots 0 .. H-1 (k-slices 0 and 1) issue the loads of step kt+2
+            // into set P; slots H/2 .. 3H/2-1 (slices 1 and 2) write set 1-P
+            // to stage 1-P, published by the barrier before slice 3
             mma_step_x<FM, FN, TM, TN>(
                 P ? A1 : A0, P ? B1 : B0, An, Bn, acc, xaf, xbf, wm, wn, lane,
                 [&](auto SL) MQ_INLINE {
                     constexpr int sl = SL;
-                    if constexpr (sl < NA + NB) {
-                        if constexpr (sl < NA) la.load(P, sl);
-                        else lb.load(P, sl - NA);
+                    if constexpr (sl < H) {
+                        constexpr int lo = sl * (NA + NB) / H, hi = (sl + 1) * (NA + NB) / H;
+                        static_for<hi - lo>([&](auto O) MQ_INLINE {
+                            constexpr int o = lo + O;
+                            if constexpr (o < NA) la.load(P, o);
+                            else lb.load(P, o - NA);
+                        });
                     }
-                    if constexpr (sl >= 8 && sl < 8 + NA + NB) {
-                        constexpr int o = sl - 8;
-                        if constexpr (o < NA) la.store(1 - P, o, An);
-                        else lb.store(1 - P, o - NA, Bn);
+                    if constexpr (sl >= H / 2 && sl < H / 2 + H) {
+                        constexpr int w = sl - H / 2;
+                        constexpr int lo = w * (NA + NB) / H, hi = (w + 1) * (NA + NB) / H;
+                        static_for<hi - lo>([&](auto O) MQ_INLINE {
+                            constexpr int o = lo + O;
+                            if constexpr (o < NA) la.store(1 - P, o, An);
+                            else lb.store(1 - P, o - NA, Bn);
+                        });
                     }
                 },
                 [&]() MQ_INLINE { sync_lds(); });
