@@ -913,10 +913,11 @@ __device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN],
 // (j+1)%2 (second half).  The barrier at the end of the step publishes that
 // stage; it also orders the reads of stage j%2 before its refill at the end
 // of step j+1.  A global load thus has from its issue in step j until the
-// second half of step j+1 to arrive.  The 256 × 256 and 256 × 128 f16-cache
-// tiles move the barrier inside the step (mma_step_x): their LDS writes take
-// k-slices 1 and 2, the barrier follows, and slice 3 reads the next step's
-// first fragments from the stage just published (a load then has 1.25 steps).
+// second half of step j+1 to arrive.  The 256 × 256 and 256 × 128 tiles with
+// f16 activations move the barrier inside the step (mma_step_x): their LDS
+// writes take k-slices 1 and 2, the barrier follows, and slice 3 reads the
+// next step's first fragments from the stage just published (a load then has
+// 1.25 steps).
 // BM × BN: block tile, split over NWV waves.  NWV = 4 (2×2 waves): one wave
 // per SIMD, whose register file then holds a 128 × 128 sub-tile's 256
 // accumulators (the 256 × 256 tile) or the fused loaders' raw bytes.  NWV = 8
@@ -1017,11 +1018,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
             if (bw) lb.store(0, i, B0);
         sync_lds();
     }
-    // the f16-cache tiles whose k-slices have at least as many MFMAs as
-    // fragments (256 x 256, 256 x 128) run the step with its barrier inside
-    // (mma_step_x; the 7B down call 3.7% faster, gate|up 0.5%, q|k|v and o
-    // 0.5%): their fragment registers live across steps
-    constexpr bool XS = FMT == kFmtF16 && !XF32 && FM * FN >= FM + FN;
+    // the f16-activation tiles whose k-slices have at least as many MFMAs as
+    // fragments (256 x 256, 256 x 128; the f16 cache and the fused formats'
+    // 2 x 2 loaders) run the step with its barrier inside (mma_step_x; the 7B
+    // down call 3.7% faster, gate|up 0.5%, q|k|v and o 0.5%; fused o 2-5%):
+    // their fragment registers live across steps
+    constexpr bool XS = !XF32 && FM * FN >= FM + FN;
     half8 xaf[2][FM], xbf[2][FN];
     if constexpr (XS) load_frags<FM, FN, TM, TN>(A0, B0, 0, wm, wn, lane, xaf[0], xbf[0]);
 
@@ -1058,7 +1060,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
                         static_for<hi - lo>([&](auto O) MQ_INLINE {
                             constexpr int o = lo + O;
                             if constexpr (o < NA) la.store(1 - P, o, An);
-                            else lb.store(1 - P, o - NA, Bn);
+                            else if (bw) lb.store(1 - P, o - NA, Bn);
                         });
                     }
                 },
