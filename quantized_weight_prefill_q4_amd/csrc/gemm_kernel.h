@@ -783,25 +783,32 @@ __device__ __forceinline__ void mma_step_x(const u32x4 *Ac, const u32x4 *Bc, con
                                            const u32x4 *Bn, f32x16 (&acc)[FM][FN],
                                            half8 (&af)[2][FM], half8 (&bf)[2][FN], int wm, int wn,
                                            int lane, Slot &&slot, Mid &&mid) {
-    static_assert(FM * FN >= FM + FN, "a slice has at least as many MFMAs as fragments");
+    // the next slice's fragments in the order it first uses them (A0, B0 ..
+    // B(FN−1), A1 .. A(FM−1)); number u of them is read after MFMA u·NM/NF
+    // of the slice (one after each of the first NF MFMAs when NF <= NM)
+    constexpr int NM = FM * FN, NF = FM + FN;
     static_for<4>([&](auto KK) MQ_INLINE {
         constexpr int kk = KK, cur = kk & 1;
         __builtin_amdgcn_sched_barrier(0);
-        static_for<FM * FN>([&](auto IJ) MQ_INLINE {
+        static_for<NM>([&](auto IJ) MQ_INLINE {
             constexpr int i = IJ / FN, j = IJ % FN, n = (kk * FM + i) * FN + j;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], bf[cur][j], acc[i][j], 0,
                                                                0, 0);
-            if constexpr (IJ < FM + FN) {
-                constexpr int idx = IJ == 0 ? 0 : (IJ <= FN ? FM + IJ - 1 : IJ - FN);
-                constexpr int ks = kk < 3 ? kk + 1 : 0;
-                const u32x4 *Ar = kk < 3 ? Ac : An, *Br = kk < 3 ? Bc : Bn;
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (idx < FM)
-                    af[cur ^ 1][idx] = load_frag<FM, FN, TM, TN, idx>(Ar, Br, ks, wm, wn, lane);
-                else
-                    bf[cur ^ 1][idx - FM] = load_frag<FM, FN, TM, TN, idx>(Ar, Br, ks, wm, wn, lane);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            static_for<NF>([&](auto U) MQ_INLINE {
+                constexpr int u = U;
+                if constexpr ((NF <= NM ? u : u * NM / NF) == IJ) {
+                    constexpr int idx = u == 0 ? 0 : (u <= FN ? FM + u - 1 : u - FN);
+                    constexpr int ks = kk < 3 ? kk + 1 : 0;
+                    const u32x4 *Ar = kk < 3 ? Ac : An, *Br = kk < 3 ? Bc : Bn;
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (idx < FM)
+                        af[cur ^ 1][idx] = load_frag<FM, FN, TM, TN, idx>(Ar, Br, ks, wm, wn, lane);
+                    else
+                        bf[cur ^ 1][idx - FM] =
+                            load_frag<FM, FN, TM, TN, idx>(Ar, Br, ks, wm, wn, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
             if constexpr (n & 1) {
                 __builtin_amdgcn_sched_barrier(0);
                 slot(std::integral_constant<int, n / 2>());
@@ -913,11 +920,11 @@ __device__ __forceinline__ void store_tile(const Args &a, f32x16 (&acc)[FM][FN],
 // (j+1)%2 (second half).  The barrier at the end of the step publishes that
 // stage; it also orders the reads of stage j%2 before its refill at the end
 // of step j+1.  A global load thus has from its issue in step j until the
-// second half of step j+1 to arrive.  The 256 × 256 and 256 × 128 tiles with
-// f16 activations move the barrier inside the step (mma_step_x): their LDS
-// writes take k-slices 1 and 2, the barrier follows, and slice 3 reads the
-// next step's first fragments from the stage just published (a load then has
-// 1.25 steps).
+// second half of step j+1 to arrive.  The tiles with f16 activations and at
+// least two MFMAs per wave and k-slice move the barrier inside the step
+// (mma_step_x): their LDS writes take k-slices 1 and 2, the barrier follows,
+// and slice 3 reads the next step's first fragments from the stage just
+// published (a load then has 1.25 steps).
 // BM × BN: block tile, split over NWV waves.  NWV = 4 (2×2 waves): one wave
 // per SIMD, whose register file then holds a 128 × 128 sub-tile's 256
 // accumulators (the 256 × 256 tile) or the fused loaders' raw bytes.  NWV = 8
@@ -1018,12 +1025,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
             if (bw) lb.store(0, i, B0);
         sync_lds();
     }
-    // the f16-activation tiles whose k-slices have at least as many MFMAs as
-    // fragments (256 x 256, 256 x 128; the f16 cache and the fused formats'
-    // 2 x 2 loaders) run the step with its barrier inside (mma_step_x; the 7B
-    // down call 3.7% faster, gate|up 0.5%, q|k|v and o 0.5%; fused o 2-5%):
-    // their fragment registers live across steps
-    constexpr bool XS = !XF32 && FM * FN >= FM + FN;
+    // the f16-activation tiles with at least two MFMAs per wave and k-slice
+    // (all but 64 x 128; the f16 cache and the fused formats' 2 x 2 loaders)
+    // run the step with its barrier inside (mma_step_x; the 7B down call 3.7%
+    // faster, gate|up 0.5%, q|k|v and o 0.5%; fused o 2-5%, 128-row fused
+    // Q6_K at M = 128 1.5%; 64 x 128 measured 0.5% slower): their fragment
+    // registers live across steps
+    constexpr bool XS = !XF32 && FM * FN >= 2;
     half8 xaf[2][FM], xbf[2][FN];
     if constexpr (XS) load_frags<FM, FN, TM, TN>(A0, B0, 0, wm, wn, lane, xaf[0], xbf[0]);
 
