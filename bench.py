@@ -388,7 +388,13 @@ def sweep(torch, mq, dev, log_rows):
         for M in ms:
             measure(M)
         cross = crossover()
-        out[name] = {"crossover_M": cross, "by_M": {m: res[m] for m in sorted(res)}}
+        # points where the two paths are within 3% of each other: there the
+        # order can flip from run to run (box, clock), and so can the crossover
+        ties = [m for m in sorted(res)
+                if abs(res[m]["cache_us"] - res[m]["fused_us"])
+                <= 0.03 * min(res[m]["cache_us"], res[m]["fused_us"])]
+        out[name] = {"crossover_M": cross, "within_3pct_M": ties,
+                     "by_M": {m: res[m] for m in sorted(res)}}
         del caches, qs, cache0, q0
         torch.cuda.empty_cache()
     return out
@@ -1179,6 +1185,8 @@ def main():
             log(r)
         log("  crossover M (smallest M where the cache GEMM is faster): " +
             ", ".join(f"{k}: {v['crossover_M']}" for k, v in cross.items()))
+        log("  M where the two paths are within 3%: " +
+            ", ".join(f"{k}: {v['within_3pct_M'] or '-'}" for k, v in cross.items()))
 
     # -- every weight format on one shape ------------------------------------------------
     fmts = None
