@@ -8,9 +8,10 @@ wrappers only check dtypes/devices/strides and pass pointers.
 
 from __future__ import annotations
 
-import torch
-
 import ctypes
+import functools
+
+import torch
 
 from ._lib import (MQ_Q4_0, MQ_Q4_K, MQ_Q5_0, MQ_Q5_1, MQ_Q5_K, MQ_Q6_K, MQ_Q8_0,
                    MqDequantJob, MqGemmPlanInfo, check, lib)
@@ -52,16 +53,37 @@ def _need_shape(t: torch.Tensor, rows: int, cols: int, name: str) -> None:
 def _need_span(t: torch.Tensor, elems: int, name: str) -> None:
     """t's storage holds `elems` elements from t's first one (rows written at
     the full row stride, e.g. a cache's pad columns)."""
+    if t.is_contiguous() and t.numel() >= elems:   # its own elements suffice
+        return
     have = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
     if have < elems:
         raise ValueError(f"{name} spans {have} elements, {elems} needed")
+
+
+# The library's host-only answers (format tables, the stride rule, workspace
+# sizes) depend on their arguments alone: each is asked once per argument
+# tuple, so a call's checks make no extra round trip into the library.
+@functools.lru_cache(maxsize=4096)
+def _row_bytes(f: int, K: int) -> int:
+    return check(lib().mq_row_bytes(f, K), "mq_row_bytes")
+
+
+@functools.lru_cache(maxsize=1024)
+def _cache_ld(K: int) -> int:
+    return check(lib().mq_f16cache_ld(K), "mq_f16cache_ld")
+
+
+@functools.lru_cache(maxsize=4096)
+def _workspace_bytes(f: int, M: int, N: int, K: int, split_k: int, x_f32: bool) -> int:
+    fn = "mq_gemm_xf32_workspace_bytes" if x_f32 else "mq_gemm_workspace_bytes"
+    return check(getattr(lib(), fn)(f, M, N, K, split_k), fn)
 
 
 def _need_quant(wq: torch.Tensor, f: int, N: int, K: int) -> None:
     _need_cuda(wq, "wq", torch.uint8)
     if not wq.is_contiguous():
         raise ValueError("wq must be contiguous")
-    need = N * check(lib().mq_row_bytes(f, K), "mq_row_bytes")
+    need = N * _row_bytes(f, K)
     if wq.numel() < need:
         raise ValueError(f"wq holds {wq.numel()} bytes; {N} rows of K = {K} need {need}")
 
@@ -75,19 +97,18 @@ def block_bytes(fmt) -> int:
 
 
 def row_bytes(fmt, K: int) -> int:
-    return check(lib().mq_row_bytes(_fmt(fmt), K), "mq_row_bytes")
+    return _row_bytes(_fmt(fmt), int(K))
 
 
 def cache_ld(K: int) -> int:
-    return check(lib().mq_f16cache_ld(K), "mq_f16cache_ld")
+    return _cache_ld(int(K))
 
 
 def workspace_bytes(fmt, M: int, N: int, K: int, split_k: int = 0, x_f32: bool = False) -> int:
     """Workspace bytes of a GEMM (fmt 0 / "f16": the f16 cache); x_f32 for f32
     activations."""
     f = 0 if fmt in (0, None, "f16") else _fmt(fmt)
-    fn = "mq_gemm_xf32_workspace_bytes" if x_f32 else "mq_gemm_workspace_bytes"
-    return check(getattr(lib(), fn)(f, M, N, K, split_k), fn)
+    return _workspace_bytes(f, int(M), int(N), int(K), int(split_k), bool(x_f32))
 
 
 def gemm_plan(fmt, M: int, N: int, K: int, split_k: int = 0, path: str = "f16") -> dict:
