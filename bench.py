@@ -283,7 +283,7 @@ def load_phase(torch, mq, W, reps):
     graph holding it, best ms over `reps` eager calls, per-call records of one
     extra pass of single-matrix calls with HIP events around each call).  The
     eager figure also holds the binding's host-side check of the 196 jobs,
-    during which the GPU idles after the first event (~0.6 ms)."""
+    during which the GPU idles after the first event (~0.5 ms)."""
     calls = [(name, fmt, N, K, q, cache) for row in W for name, (fmt, N, K, q, cache) in row.items()]
     jobs = [(q, fmt, N, K, cache) for name, fmt, N, K, q, cache in calls]
 
